@@ -1,0 +1,107 @@
+// C entry points: context, argument validation, error reporting, dispatch to
+// the HIP launchers. Nothing here touches device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "segkv_internal.h"
+
+namespace segkv {
+
+namespace {
+thread_local char g_error[512] = "";
+}
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+}  // namespace segkv
+
+using segkv::fail;
+
+extern "C" const char *segkv_last_error(void) { return segkv::g_error; }
+
+extern "C" const char *segkv_version(void) { return "segkv 0.1 gfx950"; }
+
+extern "C" int segkv_create(const segkv_config *cfg, segkv_ctx **out)
+{
+    segkv::clear_error();
+    if (!cfg || !out) return fail(SEGKV_ERR_INVALID_ARG, "create: null argument");
+    *out = nullptr;
+    if (cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+        return fail(SEGKV_ERR_INVALID_ARG, "create: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    cfg->num_q_heads, cfg->num_kv_heads);
+    if (!segkv::supported_head_dim(cfg->head_dim))
+        return fail(SEGKV_ERR_UNSUPPORTED, "create: head_dim %d not supported (64, 128)", cfg->head_dim);
+    if (!segkv::supported_page_size(cfg->page_size))
+        return fail(SEGKV_ERR_UNSUPPORTED, "create: page_size %d not supported (16, 32, 64, 128, 256)",
+                    cfg->page_size);
+    if (cfg->num_pages < 1 || cfg->num_pages > (int64_t{1} << 31) - 1)
+        return fail(SEGKV_ERR_INVALID_ARG, "create: num_pages must be in [1, 2^31)");
+    if (!cfg->k_pool || !cfg->v_pool) return fail(SEGKV_ERR_INVALID_ARG, "create: null pool pointer");
+    segkv_ctx *ctx = new (std::nothrow) segkv_ctx;
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "create: out of host memory");
+    ctx->cfg = *cfg;
+    *out = ctx;
+    return SEGKV_OK;
+}
+
+extern "C" void segkv_destroy(segkv_ctx *ctx) { delete ctx; }
+
+extern "C" int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new, int64_t num_rows,
+                                 const int32_t *cu_rows, const int32_t *pos0, const int32_t *page_of,
+                                 int32_t num_seqs, int32_t max_lp, int32_t max_rows_per_seq, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "write_pages: null context");
+    if (num_seqs < 1 || max_lp < 1 || max_rows_per_seq < 0 || num_rows < 0)
+        return fail(SEGKV_ERR_INVALID_ARG, "write_pages: bad sizes (num_seqs %d, max_lp %d, max_rows %d)",
+                    num_seqs, max_lp, max_rows_per_seq);
+    if (num_rows == 0 || max_rows_per_seq == 0) return SEGKV_OK;
+    if (!k_new || !v_new || !cu_rows || !pos0 || !page_of)
+        return fail(SEGKV_ERR_INVALID_ARG, "write_pages: null pointer");
+    return segkv::launch_write_pages(ctx->cfg, k_new, v_new, num_rows, cu_rows, pos0, page_of, num_seqs, max_lp,
+                                     max_rows_per_seq, stream);
+}
+
+extern "C" int segkv_gather_pages(const segkv_ctx *ctx, const int32_t *page_ids, int64_t n, void *k_out,
+                                  void *v_out, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "gather_pages: null context");
+    if (n < 0) return fail(SEGKV_ERR_INVALID_ARG, "gather_pages: negative count");
+    if (n == 0) return SEGKV_OK;
+    if (!page_ids || !k_out || !v_out) return fail(SEGKV_ERR_INVALID_ARG, "gather_pages: null pointer");
+    return segkv::launch_gather_pages(ctx->cfg, page_ids, n, k_out, v_out, stream);
+}
+
+extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
+                                  int32_t o_dtype, float *lse, float softmax_scale, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx || !t) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null argument");
+    const segkv_config &cfg = ctx->cfg;
+    if (o_dtype != SEGKV_DTYPE_F32 && o_dtype != SEGKV_DTYPE_BF16)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: o_dtype must be SEGKV_DTYPE_F32 or SEGKV_DTYPE_BF16");
+    const segkv::UnitShape shape = segkv::unit_shape(cfg.num_q_heads / cfg.num_kv_heads);
+    if (t->unit_rows != shape.rows || t->unit_heads != shape.heads)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: tables built for units of %d rows x %d heads, kernel "
+                    "uses %d x %d", t->unit_rows, t->unit_heads, shape.rows, shape.heads);
+    if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: negative table size");
+    if (t->num_units == 0) return SEGKV_OK;
+    if (!t->seg_desc || !t->page_list || !t->work || !q || !o)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null pointer");
+    float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
+    const float scale_log2 = scale * 1.44269504088896340736f;  // scores enter exp2 pre-multiplied by log2(e)
+    return segkv::launch_attn_prefill(cfg, *t, q, o, o_dtype, lse, scale_log2, stream);
+}

@@ -1,0 +1,368 @@
+// Fused variable-length SegPaged prefill attention (EXECUTE) for gfx950.
+//
+// RedKnot summary page, "SegPaged Attention": one fused varlen pass over the
+// per-(layer, KV head) page segments, with no attention-mask tensor; each
+// head only reads the pages its visible keys live in. Global heads see the
+// full causal context, local heads a sliding window ("Head-Class
+// Sparsification"). The softmax is blockwise with a running maximum carried
+// across KV blocks, the cross-block offset idea of the KV-cache management
+// page (section 5.2), and the next KV block is fetched while the current one
+// is being computed (same page, section 4.2).
+//
+// Work decomposition. One workgroup = one work unit from the host-built
+// list (longest first): `rows` consecutive query rows of one segment for
+// `heads` query heads of the segment's GQA group. Its four wavefronts each
+// own one (query head, 32-row block); all of them consume the same K/V tiles
+// from LDS, so a staged tile serves 128 query rows.
+//
+// Per KV tile of 64 keys, each wavefront computes on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   S^T[key][query] = K . Q^T     A = K rows from LDS, B = Q^T held in VGPRs
+//   O^T[d][query]  += V^T . P^T   A = V^T rows from LDS, B = P^T from S^T
+// With S^T in the accumulator layout every lane holds one query column, so
+// the row maximum and row sum are lane-local plus one exchange between the
+// two 32-lane halves, and the rescale of O is a per-lane scalar. The K rows
+// are fed to the S^T product in a swizzled order (bits 2 and 3 of the row
+// index swapped) so that each lane's S^T accumulator registers, converted to
+// bf16, are exactly the 8 consecutive keys the P^T operand of the next
+// product needs; the V pages are stored key-innermost so the matching V^T
+// operand is one 16-byte LDS read.
+//
+// Masking is index arithmetic on the tiles that cross the causal diagonal or
+// the window edge; tiles outside a wavefront's band are skipped, tiles inside
+// it run unmasked. Keys outside the segment's stored-and-visible range are
+// zero-filled in LDS so an undefined slot can never reach P.V.
+#include <hip/hip_runtime.h>
+
+#include "segkv_internal.h"
+
+namespace segkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr int kBK = kKvTile;            // keys per tile
+constexpr int kThreads = kWaves * 64;   // 256
+constexpr float kRescaleSlack = 8.0f;   // log2-domain headroom before the running max is refreshed
+constexpr float kNegBig = -1.0e30f;     // finite "no key yet" running max
+
+template <int D>
+struct Tile {
+    static constexpr int kLd = D + 8;                 // K tile row stride (elements), 16-byte padded
+    static constexpr int vLd = kBK + 8;               // V^T tile row stride (elements)
+    static constexpr int kElems = kBK * kLd;
+    static constexpr int vElems = D * vLd;
+    static constexpr int stage = kElems + vElems;     // one LDS stage: K tile + V^T tile
+    static constexpr int kPerThread = kBK * D / 8 / kThreads;   // 16-byte chunks per thread
+    static constexpr int vPerThread = D * kBK / 8 / kThreads;
+};
+
+template <int D>
+struct Staged {
+    u32x4 k[Tile<D>::kPerThread];
+    u32x4 v[Tile<D>::vPerThread];
+};
+
+// K row fed to MFMA row r: bits 2 and 3 of r swapped.
+__device__ __forceinline__ int swizzle_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Fetch one KV tile (keys tile_key0 .. tile_key0+63 of the segment) from the
+// pools into registers. Keys outside [zero_lo, zero_hi) become zeros.
+template <int D>
+__device__ __forceinline__ void fetch_tile(Staged<D> &st, const u16 *__restrict__ kpool,
+                                           const u16 *__restrict__ vpool, const int32_t *__restrict__ pages,
+                                           int32_t n_pages, int64_t num_pages, int log2P, int tile_key0,
+                                           int zero_lo, int zero_hi)
+{
+    const int pmask = (1 << log2P) - 1;
+#pragma unroll
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        const int key = c / (D / 8), dc = c % (D / 8);
+        const int idx = tile_key0 + key;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (idx >= 0 && idx >= zero_lo && idx < zero_hi) {
+            const int lpi = idx >> log2P;
+            const int page = lpi < n_pages ? pages[lpi] : -1;
+            if (page >= 0 && page < num_pages)
+                val = *reinterpret_cast<const u32x4 *>(
+                    kpool + ((static_cast<int64_t>(page) << log2P) + (idx & pmask)) * D + dc * 8);
+        }
+        st.k[r] = val;
+    }
+#pragma unroll
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        const int d = c / (kBK / 8), kc = c % (kBK / 8);
+        const int idx0 = tile_key0 + kc * 8;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (idx0 >= 0 && idx0 + 7 >= zero_lo && idx0 < zero_hi) {
+            const int lpi = idx0 >> log2P;
+            const int page = lpi < n_pages ? pages[lpi] : -1;
+            if (page >= 0 && page < num_pages) {
+                val = *reinterpret_cast<const u32x4 *>(
+                    vpool + ((static_cast<int64_t>(page) * D + d) << log2P) + (idx0 & pmask));
+                if (idx0 < zero_lo || idx0 + 8 > zero_hi) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int idx = idx0 + i;
+                        if (idx < zero_lo || idx >= zero_hi) val[i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
+                    }
+                }
+            }
+        }
+        st.v[r] = val;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict__ stage)
+{
+    u16 *ks = stage;
+    u16 *vs = stage + Tile<D>::kElems;
+#pragma unroll
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        const int key = c / (D / 8), dc = c % (D / 8);
+        *reinterpret_cast<u32x4 *>(ks + key * Tile<D>::kLd + dc * 8) = st.k[r];
+    }
+#pragma unroll
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        const int d = c / (kBK / 8), kc = c % (kBK / 8);
+        *reinterpret_cast<u32x4 *>(vs + d * Tile<D>::vLd + kc * 8) = st.v[r];
+    }
+}
+
+template <int D, int HPW, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
+    int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
+    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
+    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse)
+{
+    using T = Tile<D>;
+    constexpr int kRowBlocks = kWaves / HPW;
+    constexpr int kUnitRows = kWaveRows * kRowBlocks;
+    constexpr int kSteps = D / 16;      // MFMA k-steps over the head dim for S^T
+    constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) u16 smem[2 * T::stage];
+
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS);
+    const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
+    if (seg < 0 || seg >= num_segments) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off > num_page_entries) return;
+    int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
+    if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
+    const int32_t *pages = page_list + page_off;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const int head = head0 + wave % HPW;
+    const int wrow0 = row0 + (wave / HPW) * kWaveRows;
+
+    // Key band of the whole unit, as tile indices relative to k_pos0.
+    const int unit_end = min(row0 + kUnitRows, n_q);
+    const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
+    const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
+    const int tile_beg = (lo_pos - k_pos0) / kBK;
+    const int tile_end = (last_pos + 1 - k_pos0 + kBK - 1) / kBK;
+    // Stored keys that some query of the segment can see; everything else is zero-filled.
+    const int zero_lo = (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0;
+    const int zero_hi = k_len;
+
+    // This wavefront's rows.
+    const bool wave_valid = wrow0 < n_q && head < hq;
+    const int wrow_end = min(wrow0 + kWaveRows, n_q);
+    const int wp_lo = q_pos0 + wrow0, wp_hi = q_pos0 + wrow_end - 1;
+    const int my_t = min(wrow0 + col, n_q - 1);
+    const int my_pos = q_pos0 + my_t;
+    const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
+    const bool row_ok = wave_valid && (wrow0 + col) < n_q && my_row < total_q_rows;
+
+    bf16x8 qreg[kSteps];
+    {
+        const bool can_load = wave_valid && my_row < total_q_rows;
+        const u16 *qp = q + (my_row * hq + head) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+            qreg[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 oacc[kDBlocks];
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
+    float m = kNegBig, lsum = 0.f;
+
+    Staged<D> st;
+    fetch_tile<D>(st, kpool, vpool, pages, n_pages, num_pages, log2P, tile_beg * kBK, zero_lo, zero_hi);
+    store_tile<D>(st, smem);
+    __syncthreads();
+
+    for (int jt = tile_beg; jt < tile_end; ++jt) {
+        const int cur = (jt - tile_beg) & 1;
+        const bool more = jt + 1 < tile_end;
+        if (more)
+            fetch_tile<D>(st, kpool, vpool, pages, n_pages, num_pages, log2P, (jt + 1) * kBK, zero_lo, zero_hi);
+
+        const u16 *ks = smem + cur * T::stage;
+        const u16 *vs = ks + T::kElems;
+        const int kp0 = k_pos0 + jt * kBK;
+        const bool active = wave_valid && kp0 <= wp_hi && !(window && kp0 + kBK - 1 < wp_lo - window + 1);
+        if (active) {
+            const bool full = (kp0 + kBK - 1 <= wp_lo) && (window == 0 || kp0 >= wp_hi - window + 1);
+            // S^T = K . Q^T, two 32-key blocks.
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x16{};
+                const u16 *krow = ks + (32 * kb + swizzle_row(col)) * T::kLd + 8 * half;
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + 16 * s);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
+                }
+            }
+            if (!full) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int jj = e >> 2, ii = e & 3;
+                        const int kpos = kp0 + 32 * kb + 16 * (jj >> 1) + 8 * half + 4 * (jj & 1) + ii;
+                        const bool vis = kpos <= my_pos && (window == 0 || my_pos - kpos < window);
+                        if (!vis) sacc[kb][e] = -__builtin_inff();
+                    }
+            }
+            // Running maximum (log2 domain), refreshed only when it grows by more than the slack.
+            float mt = sacc[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+            if (__any(mt > m + kRescaleSlack)) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
+                m = m_new;
+            }
+            // P = exp2(S * scale * log2(e) - m), summed per lane, packed to bf16 B operands.
+            bf16x8 pb[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], scale_log2, -m));
+                    lsum += p;
+                    pb[2 * kb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+                }
+            // O^T += V^T . P^T, four 16-key steps.
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const u16 *vrow = vs + (32 * db + col) * T::vLd + 8 * half;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vrow + 16 * t);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], oacc[db], 0, 0, 0);
+                }
+            }
+        }
+        if (more) store_tile<D>(st, smem + (cur ^ 1) * T::stage);
+        __syncthreads();
+    }
+
+    // Epilogue: combine the two halves' row sums, normalise, store.
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (!row_ok) return;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    const int64_t obase = (my_row * hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int d0 = 32 * db + 8 * jj + 4 * half;
+            const float v0 = oacc[db][4 * jj + 0] * inv, v1 = oacc[db][4 * jj + 1] * inv;
+            const float v2 = oacc[db][4 * jj + 2] * inv, v3 = oacc[db][4 * jj + 3] * inv;
+            if constexpr (OUT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                bf16x4 w = {static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
+                            static_cast<__bf16>(v3)};
+                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) = w;
+            } else {
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
+            }
+        }
+    if (lse && half == 0)
+        lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
+}
+
+int log2_of(int p)
+{
+    int l = 0;
+    while ((1 << l) < p) ++l;
+    return l;
+}
+
+template <int D, int HPW, bool OUT_BF16>
+void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
+            hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn_prefill_kernel<D, HPW, OUT_BF16>), dim3(static_cast<unsigned>(t.num_units)),
+                       dim3(kThreads), 0, stream, static_cast<const u16 *>(q), static_cast<const u16 *>(cfg.k_pool),
+                       static_cast<const u16 *>(cfg.v_pool), cfg.num_pages, log2_of(cfg.page_size), t.seg_desc,
+                       t.page_list, t.num_page_entries, t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads,
+                       scale_log2, o, lse);
+}
+
+template <int D, int HPW>
+void launch_dtype(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
+                  float *lse, float scale_log2, hipStream_t stream)
+{
+    if (o_dtype == SEGKV_DTYPE_BF16)
+        launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, stream);
+    else
+        launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, stream);
+}
+
+template <int D>
+void launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
+                  float *lse, float scale_log2, hipStream_t stream)
+{
+    switch (t.unit_heads) {
+    case 4: launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
+    case 2: launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
+    default: launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
+    }
+}
+
+}  // namespace
+
+int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
+                        int32_t o_dtype, float *lse, float scale_log2, void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cfg.head_dim == 128)
+        launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, s);
+    else
+        launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, s);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: %s", hipGetErrorString(err));
+    return SEGKV_OK;
+}
+
+}  // namespace segkv

@@ -1,0 +1,49 @@
+// Internal declarations shared by the host C++ and the HIP translation units.
+#pragma once
+
+#include "segkv.h"
+
+struct segkv_ctx {
+    segkv_config cfg;
+};
+
+namespace segkv {
+
+// Record a message for segkv_last_error() and return code.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Keys per KV tile of the attention kernel (one LDS stage).
+constexpr int kKvTile = 64;
+// Query rows handled by one wavefront (one 32-wide MFMA column block).
+constexpr int kWaveRows = 32;
+// Wavefronts per attention workgroup.
+constexpr int kWaves = 4;
+
+// Shape of one attention work unit for a given GQA group size G: the
+// workgroup's four wavefronts cover `heads` query heads of one group times
+// `rows` query rows, one (head, 32-row block) per wavefront.
+struct UnitShape {
+    int rows;
+    int heads;
+};
+inline UnitShape unit_shape(int G)
+{
+    int heads = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    return UnitShape{kWaveRows * (kWaves / heads), heads};
+}
+
+inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
+inline bool supported_page_size(int p) { return p == 16 || p == 32 || p == 64 || p == 128 || p == 256; }
+
+// Kernel launchers (segkv_kernels.hip). They assume validated arguments and
+// return SEGKV_OK or SEGKV_ERR_HIP.
+int launch_write_pages(const segkv_config &cfg, const void *k_new, const void *v_new, int64_t num_rows,
+                       const int32_t *cu_rows, const int32_t *pos0, const int32_t *page_of, int32_t num_seqs,
+                       int32_t max_lp, int32_t max_rows_per_seq, void *stream);
+int launch_gather_pages(const segkv_config &cfg, const int32_t *page_ids, int64_t n, void *k_out, void *v_out,
+                        void *stream);
+int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
+                        int32_t o_dtype, float *lse, float scale_log2, void *stream);
+
+}  // namespace segkv

@@ -1,0 +1,185 @@
+// Host-side head-class page-table builder (SELECTVISIBLESTATE).
+//
+// RedKnot summary page, "Head-Class Sparsification" and "SegPaged Attention":
+// every (layer, KV head) carries an offline class; a global head keeps the
+// full causal context, a local head keeps a sliding window, and each head
+// physically keeps only the pages its visible keys live in. This file turns
+// one layer's class table, sequence lengths and block table (the
+// logical-to-physical page map of the KV-cache management page, section 3.1)
+// into the flat arrays the attention kernel reads, plus the kernel's work
+// list ordered longest-first.
+#include <algorithm>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+#include "segkv_internal.h"
+
+namespace {
+
+struct Seg {
+    int32_t q_row0, n_q, q_pos0, kv_head, window, k_pos0, k_len, page_off;
+    int32_t first_lp, n_pages;
+    int64_t pairs;
+};
+
+// Sum over the n new rows i = c .. c+n-1 of the number of visible keys,
+// min(i + 1, W) for a local head (W > 0) or i + 1 for a global head (W == 0).
+int64_t visible_pairs(int64_t c, int64_t n, int64_t W)
+{
+    const int64_t a = c + 1;  // visible keys of the first new row, before the window cap
+    if (W == 0) return n * a + n * (n - 1) / 2;
+    if (a >= W) return n * W;
+    const int64_t k = std::min<int64_t>(n, W - a);  // rows still below the cap
+    return k * a + k * (k - 1) / 2 + (n - k) * W;
+}
+
+}  // namespace
+
+extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_inputs *in, segkv_tables *out)
+{
+    using segkv::fail;
+    segkv::clear_error();
+    if (!ctx || !in || !out) return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: null argument");
+    const segkv_config &cfg = ctx->cfg;
+    const int32_t hq = cfg.num_q_heads, hkv = cfg.num_kv_heads, P = cfg.page_size;
+    const int32_t G = hq / hkv;
+    const int32_t S = in->num_seqs;
+    if (S < 1) return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: num_seqs must be >= 1");
+    if (in->max_lp < 1) return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: max_lp must be >= 1");
+    if (!in->cached_len || !in->new_len || !in->head_class || !in->window || !in->page_of)
+        return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: null input array");
+    if (static_cast<int64_t>(S) * hkv > std::numeric_limits<int32_t>::max())
+        return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: too many segments");
+
+    const segkv::UnitShape shape = segkv::unit_shape(G);
+    std::vector<Seg> segs;
+    segs.reserve(static_cast<size_t>(S) * hkv);
+    int64_t q_rows = 0, pages = 0, units = 0, total_pairs = 0;
+
+    for (int32_t b = 0; b < S; ++b) {
+        const int64_t c = in->cached_len[b], n = in->new_len[b];
+        if (c < 0 || n < 1)
+            return fail(SEGKV_ERR_INVALID_ARG, "sequence %d: need cached_len >= 0 and new_len >= 1", b);
+        const int64_t T = c + n;
+        if (T > std::numeric_limits<int32_t>::max() || q_rows + n > std::numeric_limits<int32_t>::max())
+            return fail(SEGKV_ERR_INVALID_ARG, "sequence %d: length overflows int32", b);
+        for (int32_t g = 0; g < hkv; ++g) {
+            Seg sg{};
+            const bool global = in->head_class[g] != 0;
+            int64_t first_pos = 0;
+            if (!global) {
+                const int64_t W = in->window[g];
+                if (W < 1) return fail(SEGKV_ERR_INVALID_ARG, "kv head %d: local window must be >= 1", g);
+                first_pos = (std::max<int64_t>(0, c - W + 1) / P) * P;
+                sg.window = static_cast<int32_t>(W);
+            }
+            const int64_t first_lp = first_pos / P, last_lp = (T - 1) / P;
+            if (last_lp >= in->max_lp)
+                return fail(SEGKV_ERR_OUT_OF_RANGE, "sequence %d needs logical page %lld >= max_lp %d", b,
+                            static_cast<long long>(last_lp), in->max_lp);
+            const int32_t *row = in->page_of + (static_cast<int64_t>(b) * hkv + g) * in->max_lp;
+            for (int64_t lp = first_lp; lp <= last_lp; ++lp) {
+                const int32_t id = row[lp];
+                if (id < 0 || id >= cfg.num_pages)
+                    return fail(SEGKV_ERR_OUT_OF_RANGE, "segment (seq %d, kv head %d) logical page %lld: id %d "
+                                "outside [0, %lld)", b, g, static_cast<long long>(lp), id,
+                                static_cast<long long>(cfg.num_pages));
+            }
+            sg.q_row0 = static_cast<int32_t>(q_rows);
+            sg.n_q = static_cast<int32_t>(n);
+            sg.q_pos0 = static_cast<int32_t>(c);
+            sg.kv_head = g;
+            sg.k_pos0 = static_cast<int32_t>(first_pos);
+            sg.k_len = static_cast<int32_t>(T - first_pos);
+            sg.page_off = static_cast<int32_t>(pages);
+            sg.first_lp = static_cast<int32_t>(first_lp);
+            sg.n_pages = static_cast<int32_t>(last_lp - first_lp + 1);
+            sg.pairs = G * visible_pairs(c, n, sg.window);
+            pages += sg.n_pages;
+            if (pages > std::numeric_limits<int32_t>::max())
+                return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: page list exceeds int32 offsets");
+            total_pairs += sg.pairs;
+            units += ((n + shape.rows - 1) / shape.rows) * (G / shape.heads);
+            segs.push_back(sg);
+        }
+        q_rows += n;
+    }
+    if (units > std::numeric_limits<int32_t>::max())
+        return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: too many work units");
+
+    const int32_t nseg = static_cast<int32_t>(segs.size());
+    out->num_segments = nseg;
+    out->num_units = static_cast<int32_t>(units);
+    out->num_page_entries = pages;
+    out->total_pairs = total_pairs;
+    out->total_q_rows = static_cast<int32_t>(q_rows);
+    out->unit_rows = shape.rows;
+    out->unit_heads = shape.heads;
+    if (out->seg_cap < nseg || out->seq_cap < S || out->page_cap < pages || out->unit_cap < units)
+        return fail(SEGKV_ERR_CAPACITY, "build_head_tables: buffers too small (need %d segments, %d sequences, "
+                    "%lld page entries, %lld units)", nseg, S, static_cast<long long>(pages),
+                    static_cast<long long>(units));
+    if (!out->seg_desc || !out->cu_seqlens_q || !out->cu_seqlens_k || !out->cu_pages || !out->page_list ||
+        !out->pairs || !out->work)
+        return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: null output buffer");
+
+    // Segment arrays, prefix sums and the page list.
+    int64_t k_acc = 0;
+    out->cu_seqlens_k[0] = 0;
+    out->cu_pages[0] = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        const Seg &sg = segs[s];
+        int32_t *d = out->seg_desc + static_cast<int64_t>(s) * SEGKV_SEG_FIELDS;
+        d[SEGKV_SEG_Q_ROW0] = sg.q_row0;
+        d[SEGKV_SEG_N_Q] = sg.n_q;
+        d[SEGKV_SEG_Q_POS0] = sg.q_pos0;
+        d[SEGKV_SEG_KV_HEAD] = sg.kv_head;
+        d[SEGKV_SEG_WINDOW] = sg.window;
+        d[SEGKV_SEG_K_POS0] = sg.k_pos0;
+        d[SEGKV_SEG_K_LEN] = sg.k_len;
+        d[SEGKV_SEG_PAGE_OFF] = sg.page_off;
+        k_acc += sg.k_len;
+        if (k_acc > std::numeric_limits<int32_t>::max())
+            return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: cu_seqlens_k overflows int32");
+        out->cu_seqlens_k[s + 1] = static_cast<int32_t>(k_acc);
+        out->cu_pages[s + 1] = sg.page_off + sg.n_pages;
+        out->pairs[s] = sg.pairs;
+        const int32_t b = s / hkv;
+        const int32_t *row = in->page_of + static_cast<int64_t>(s) * in->max_lp;
+        (void)b;
+        std::memcpy(out->page_list + sg.page_off, row + sg.first_lp, sizeof(int32_t) * sg.n_pages);
+    }
+    out->cu_seqlens_q[0] = 0;
+    for (int32_t b = 0; b < S; ++b) out->cu_seqlens_q[b + 1] = out->cu_seqlens_q[b] + in->new_len[b];
+
+    // Work list: every (segment, row block, head block) once, with its cost in
+    // KV tiles; then longest first, ties in generation order.
+    struct Unit {
+        int32_t seg, row0, head0, tiles;
+    };
+    std::vector<Unit> list;
+    list.reserve(static_cast<size_t>(units));
+    for (int32_t s = 0; s < nseg; ++s) {
+        const Seg &sg = segs[s];
+        for (int32_t r0 = 0; r0 < sg.n_q; r0 += shape.rows) {
+            const int64_t first = static_cast<int64_t>(sg.q_pos0) + r0;
+            const int64_t last = static_cast<int64_t>(sg.q_pos0) + std::min(r0 + shape.rows, sg.n_q) - 1;
+            const int64_t lo = sg.window == 0 ? 0 : std::max<int64_t>(0, first - sg.window + 1);
+            const int64_t kbeg = lo - sg.k_pos0, kend = last + 1 - sg.k_pos0;
+            const int32_t tiles = static_cast<int32_t>((kend + segkv::kKvTile - 1) / segkv::kKvTile -
+                                                       kbeg / segkv::kKvTile);
+            for (int32_t h = 0; h < G; h += shape.heads)
+                list.push_back(Unit{s, r0, sg.kv_head * G + h, tiles});
+        }
+    }
+    std::stable_sort(list.begin(), list.end(), [](const Unit &a, const Unit &b) { return a.tiles > b.tiles; });
+    for (size_t u = 0; u < list.size(); ++u) {
+        int32_t *w = out->work + u * SEGKV_UNIT_FIELDS;
+        w[SEGKV_UNIT_SEGMENT] = list[u].seg;
+        w[SEGKV_UNIT_ROW0] = list[u].row0;
+        w[SEGKV_UNIT_HEAD0] = list[u].head0;
+        w[SEGKV_UNIT_TILES] = list[u].tiles;
+    }
+    return SEGKV_OK;
+}

@@ -1,0 +1,240 @@
+"""Python binding of libsegkv (argument marshalling only).
+
+Every function forwards to the C entry point of the same name declared in
+include/segkv.h. Torch tensors are used only as device memory and for the
+current HIP stream; all computation runs in the library's kernels. There is
+no fallback: if libsegkv.so is missing, importing this module raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsegkv.so")
+
+SEGKV_OK = 0
+SEGKV_ERR_INVALID_ARG = -1
+SEGKV_ERR_OUT_OF_RANGE = -2
+SEGKV_ERR_CAPACITY = -3
+SEGKV_ERR_HIP = -4
+SEGKV_ERR_UNSUPPORTED = -5
+SEGKV_DTYPE_F32 = 0
+SEGKV_DTYPE_BF16 = 1
+SEG_FIELDS = 8
+UNIT_FIELDS = 4
+SEG_FIELD_NAMES = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len", "page_off")
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class segkv_config(ctypes.Structure):
+    _fields_ = [("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32), ("page_size", _i32),
+                ("num_pages", _i64), ("k_pool", _P), ("v_pool", _P)]
+
+
+class segkv_table_inputs(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("max_lp", _i32), ("cached_len", _P), ("new_len", _P),
+                ("head_class", _P), ("window", _P), ("page_of", _P)]
+
+
+class segkv_tables(ctypes.Structure):
+    _fields_ = [("seg_cap", _i32), ("seq_cap", _i32), ("page_cap", _i64), ("unit_cap", _i32),
+                ("num_segments", _i32), ("num_units", _i32), ("num_page_entries", _i64), ("total_pairs", _i64),
+                ("total_q_rows", _i32), ("unit_rows", _i32), ("unit_heads", _i32),
+                ("seg_desc", _P), ("cu_seqlens_q", _P), ("cu_seqlens_k", _P), ("cu_pages", _P),
+                ("page_list", _P), ("pairs", _P), ("work", _P)]
+
+
+class segkv_dev_tables(ctypes.Structure):
+    _fields_ = [("seg_desc", _P), ("page_list", _P), ("work", _P), ("num_segments", _i32), ("num_units", _i32),
+                ("num_page_entries", _i64), ("total_q_rows", _i32), ("unit_rows", _i32), ("unit_heads", _i32)]
+
+
+class SegKVError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"segkv error {code}: {message}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m head_segmented_paged_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "segkv_create": ([ctypes.POINTER(segkv_config), ctypes.POINTER(_P)], ctypes.c_int),
+        "segkv_destroy": ([_P], None),
+        "segkv_write_pages": ([_P, _P, _P, _i64, _P, _P, _P, _i32, _i32, _i32, _P], ctypes.c_int),
+        "segkv_build_head_tables": ([_P, ctypes.POINTER(segkv_table_inputs), ctypes.POINTER(segkv_tables)],
+                                    ctypes.c_int),
+        "segkv_attn_prefill": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P],
+                               ctypes.c_int),
+        "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
+        "segkv_last_error": ([], ctypes.c_char_p),
+        "segkv_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
+            "segkv_attn_prefill", "segkv_gather_pages", "segkv_last_error", "segkv_version")
+
+
+def segkv_last_error() -> str:
+    return _lib.segkv_last_error().decode()
+
+
+def segkv_version() -> str:
+    return _lib.segkv_version().decode()
+
+
+def _check(rc):
+    if rc != SEGKV_OK:
+        raise SegKVError(rc, segkv_last_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data_as(ctypes.c_void_p)
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Context:
+    """Owns a segkv_ctx and keeps the pool tensors alive."""
+
+    def __init__(self, handle, cfg, k_pool, v_pool):
+        self.handle = handle
+        self.cfg = cfg
+        self.k_pool = k_pool
+        self.v_pool = v_pool
+
+    @property
+    def G(self):
+        return self.cfg.num_q_heads // self.cfg.num_kv_heads
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib.segkv_destroy(self.handle)
+            self.handle = None
+
+
+def segkv_create(k_pool, v_pool, num_q_heads, num_kv_heads, head_dim, page_size, num_pages=None):
+    """k_pool: bf16 [num_pages][page_size][head_dim]; v_pool: bf16 [num_pages][head_dim][page_size]."""
+    if num_pages is None:
+        num_pages = k_pool.shape[0] if k_pool is not None else 0
+    cfg = segkv_config(num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                       _ptr(k_pool) if k_pool is not None else None,
+                       _ptr(v_pool) if v_pool is not None else None)
+    h = ctypes.c_void_p()
+    _check(_lib.segkv_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return Context(h, cfg, k_pool, v_pool)
+
+
+def segkv_destroy(ctx: Context):
+    if ctx.handle:
+        _lib.segkv_destroy(ctx.handle)
+        ctx.handle = None
+
+
+def segkv_write_pages(ctx, k_new, v_new, cu_rows, pos0, page_of, max_rows_per_seq, stream=None):
+    """k_new/v_new bf16 [rows][hkv][D]; cu_rows [S+1], pos0 [S], page_of [S][hkv][max_lp]: device int32."""
+    num_seqs = pos0.shape[0]
+    max_lp = page_of.shape[-1]
+    _check(_lib.segkv_write_pages(ctx.handle, _ptr(k_new), _ptr(v_new), k_new.shape[0], _ptr(cu_rows),
+                                  _ptr(pos0), _ptr(page_of), num_seqs, max_lp, int(max_rows_per_seq),
+                                  _stream(stream)))
+
+
+def segkv_build_head_tables(ctx, cached_len, new_len, head_class, window, page_of):
+    """Host arrays in, dict of host numpy arrays out (see segkv_tables in the header)."""
+    c = np.ascontiguousarray(cached_len, dtype=np.int32)
+    n = np.ascontiguousarray(new_len, dtype=np.int32)
+    cls = np.ascontiguousarray(head_class, dtype=np.int8)
+    win = np.ascontiguousarray(window, dtype=np.int32)
+    po = np.ascontiguousarray(page_of, dtype=np.int32)
+    inp = segkv_table_inputs(c.shape[0], po.shape[-1], _ptr(c), _ptr(n), _ptr(cls), _ptr(win), _ptr(po))
+    out = segkv_tables()
+    rc = _lib.segkv_build_head_tables(ctx.handle, ctypes.byref(inp), ctypes.byref(out))
+    if rc not in (SEGKV_OK, SEGKV_ERR_CAPACITY):
+        _check(rc)
+    S = out.num_segments
+    bufs = {
+        "seg_desc": np.zeros((S, SEG_FIELDS), np.int32),
+        "cu_seqlens_q": np.zeros(c.shape[0] + 1, np.int32),
+        "cu_seqlens_k": np.zeros(S + 1, np.int32),
+        "cu_pages": np.zeros(S + 1, np.int32),
+        "page_list": np.zeros(max(out.num_page_entries, 1), np.int32),
+        "pairs": np.zeros(S, np.int64),
+        "work": np.zeros((max(out.num_units, 1), UNIT_FIELDS), np.int32),
+    }
+    out2 = segkv_tables(S, c.shape[0], bufs["page_list"].shape[0], bufs["work"].shape[0])
+    for k, v in bufs.items():
+        setattr(out2, k, _ptr(v))
+    _check(_lib.segkv_build_head_tables(ctx.handle, ctypes.byref(inp), ctypes.byref(out2)))
+    res = dict(bufs)
+    res["page_list"] = res["page_list"][:out2.num_page_entries]
+    res["work"] = res["work"][:out2.num_units]
+    for i, name in enumerate(SEG_FIELD_NAMES):
+        res[name] = res["seg_desc"][:, i].copy()
+    for k in ("num_segments", "num_units", "num_page_entries", "total_pairs", "total_q_rows",
+              "unit_rows", "unit_heads"):
+        res[k] = int(getattr(out2, k))
+    return res
+
+
+class DevTables:
+    """Device copies of one layer's tables plus the struct handed to the kernel."""
+
+    def __init__(self, host, device):
+        import torch
+        self.seg_desc = torch.from_numpy(np.ascontiguousarray(host["seg_desc"])).to(device)
+        pl = host["page_list"] if host["page_list"].size else np.zeros(1, np.int32)
+        self.page_list = torch.from_numpy(np.ascontiguousarray(pl)).to(device)
+        wk = host["work"] if host["work"].size else np.zeros((1, UNIT_FIELDS), np.int32)
+        self.work = torch.from_numpy(np.ascontiguousarray(wk)).to(device)
+        self.host = host
+        self.struct = segkv_dev_tables(_ptr(self.seg_desc), _ptr(self.page_list), _ptr(self.work),
+                                       host["num_segments"], host["num_units"], host["num_page_entries"],
+                                       host["total_q_rows"], host["unit_rows"], host["unit_heads"])
+
+
+def upload_tables(host, device="cuda"):
+    return DevTables(host, device)
+
+
+def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None):
+    """q bf16 [rows][hq][D]; o fp32 or bf16 [rows][hq][D]; lse fp32 [hq][rows] or None."""
+    import torch
+    if o.dtype == torch.float32:
+        dt = SEGKV_DTYPE_F32
+    elif o.dtype == torch.bfloat16:
+        dt = SEGKV_DTYPE_BF16
+    else:
+        raise TypeError("o must be float32 or bfloat16")
+    _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
+                                   _ptr(lse), float(softmax_scale), _stream(stream)))
+
+
+def segkv_gather_pages(ctx, page_ids, k_out, v_out, stream=None):
+    """page_ids device int32 [n]; k_out/v_out bf16 [n][P][D]."""
+    _check(_lib.segkv_gather_pages(ctx.handle, _ptr(page_ids), page_ids.shape[0], _ptr(k_out), _ptr(v_out),
+                                   _stream(stream)))

@@ -1,0 +1,240 @@
+/*
+ * segkv — head-segmented paged KV cache and fused variable-length prefill
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (RedKnot summary page, sections "Head-Class Sparsification" and
+ * "SegPaged Attention"): instead of one dense [B, H, L, D] tensor, the KV
+ * cache is stored as fixed-size pages segmented per (layer, KV head). Each
+ * (layer, KV head) is labelled offline as global (keeps and attends to the
+ * full causal context) or local (keeps and attends to a sliding window).
+ * A single fused variable-length attention pass then runs causal prefill
+ * over every head's visible key set, with no attention-mask tensor. The same
+ * page records the runtime's adapter split; this library provides three of
+ * them:
+ *   BUILDSTATE          -> segkv_write_pages       (paged KV write)
+ *   SELECTVISIBLESTATE  -> segkv_build_head_tables (per-head page tables)
+ *   EXECUTE             -> segkv_attn_prefill      (fused varlen attention)
+ * Fixed-size pages with a logical-to-physical map are the PagedAttention
+ * scheme summarised on the KV-cache management page (section 3.1).
+ *
+ * Definitions used throughout
+ *   S sequences b = 0..S-1, each with c_b cached tokens (positions
+ *   0..c_b-1, already in the pool) and n_b >= 1 new tokens (positions
+ *   c_b..T_b-1, T_b = c_b + n_b) whose queries are computed.
+ *   hq query heads, hkv KV heads, G = hq / hkv; query head h reads KV head
+ *   h / G (contiguous GQA groups).
+ *   A local head with window W lets query position i see keys j with
+ *   i - W < j <= i (the W newest keys, itself included); a global head lets
+ *   it see 0 <= j <= i.
+ *   One layer's segments are s = b * hkv + g.
+ *
+ * Ownership and execution model
+ *   The caller owns every device buffer (pools, Q, O, LSE, device copies of
+ *   the tables). The library never allocates or frees device memory and never
+ *   synchronises: GPU work is enqueued on the caller's hipStream_t, passed as
+ *   void* (NULL = the null stream). A context holds only a host copy of its
+ *   configuration. Functions are thread-safe except that a context must not
+ *   be destroyed while in use.
+ *
+ * Errors
+ *   Every int-returning call returns SEGKV_OK (0) or a negative code below;
+ *   segkv_last_error() then returns a thread-local message. All argument
+ *   checks run on the host before anything is enqueued. Device-side metadata
+ *   (page ids, row offsets) is bounds-checked inside the kernels: an entry
+ *   out of range is skipped (write) or read as zeros (attention), never
+ *   dereferenced.
+ */
+#ifndef SEGKV_H
+#define SEGKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SEGKV_OK = 0,
+    SEGKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, n_b < 1, W < 1, hq % hkv != 0 ... */
+    SEGKV_ERR_OUT_OF_RANGE = -2, /* a page id needed by a visible range is -1 or >= num_pages */
+    SEGKV_ERR_CAPACITY = -3,     /* an output buffer is too small; required sizes written back */
+    SEGKV_ERR_HIP = -4,          /* a HIP launch failed; the message holds HIP's error string */
+    SEGKV_ERR_UNSUPPORTED = -5   /* head_dim or page_size the kernels are not built for */
+};
+
+enum { SEGKV_DTYPE_F32 = 0, SEGKV_DTYPE_BF16 = 1 };
+
+/* Fields of one segment descriptor (int32 [num_segments][SEGKV_SEG_FIELDS]). */
+enum {
+    SEGKV_SEG_Q_ROW0 = 0,   /* first row of this sequence in Q / O */
+    SEGKV_SEG_N_Q = 1,      /* n_b, query rows of the sequence */
+    SEGKV_SEG_Q_POS0 = 2,   /* c_b, absolute position of query row 0 */
+    SEGKV_SEG_KV_HEAD = 3,  /* g; the segment serves query heads g*G .. g*G+G-1 */
+    SEGKV_SEG_WINDOW = 4,   /* W for a local head, 0 for a global head */
+    SEGKV_SEG_K_POS0 = 5,   /* absolute position of the segment's first stored key (page aligned) */
+    SEGKV_SEG_K_LEN = 6,    /* T_b - k_pos0 keys stored for the segment */
+    SEGKV_SEG_PAGE_OFF = 7, /* offset of the segment's first page id in page_list */
+    SEGKV_SEG_FIELDS = 8
+};
+
+/* Fields of one work unit (int32 [num_units][SEGKV_UNIT_FIELDS]). A unit is
+ * one workgroup of the attention kernel: unit_rows consecutive query rows of
+ * one segment for unit_heads consecutive query heads of its GQA group. */
+enum {
+    SEGKV_UNIT_SEGMENT = 0,
+    SEGKV_UNIT_ROW0 = 1,    /* first query row, relative to the segment (0 .. n_b-1) */
+    SEGKV_UNIT_HEAD0 = 2,   /* first query head (absolute) */
+    SEGKV_UNIT_TILES = 3,   /* KV tiles the unit visits: its cost, used to order the list */
+    SEGKV_UNIT_FIELDS = 4
+};
+
+typedef struct segkv_ctx segkv_ctx;
+
+/*
+ * Pool layout (one pool shared by every layer, sequence and KV head):
+ *   k_pool: bf16 [num_pages][page_size][head_dim]  one key's head_dim values contiguous
+ *   v_pool: bf16 [num_pages][head_dim][page_size]  one dimension's page_size values contiguous
+ * Position j of a segment lives at slot j % page_size of a page. Both layouts
+ * make one page a single contiguous block (16 KiB for P = 64, D = 128); the
+ * transposed V page puts the key index innermost, which is the order the
+ * P.V contraction consumes it in.
+ */
+typedef struct segkv_config {
+    int32_t num_q_heads;   /* hq */
+    int32_t num_kv_heads;  /* hkv, hq % hkv == 0 */
+    int32_t head_dim;      /* D: 64 or 128 */
+    int32_t page_size;     /* P: 16, 32, 64, 128 or 256 */
+    int64_t num_pages;     /* pool capacity in pages */
+    void *k_pool;          /* device */
+    void *v_pool;          /* device */
+} segkv_config;
+
+/* Validate cfg and return a new context in *out (host memory only). */
+int segkv_create(const segkv_config *cfg, segkv_ctx **out);
+void segkv_destroy(segkv_ctx *ctx);
+
+/*
+ * BUILDSTATE: scatter new K/V rows of one layer into their pages.
+ *   k_new, v_new : device bf16 [num_rows][hkv][head_dim]
+ *   cu_rows      : device int32 [num_seqs+1]; rows cu_rows[b] .. cu_rows[b+1]-1
+ *                  belong to sequence b
+ *   pos0         : device int32 [num_seqs]; absolute position of row cu_rows[b]
+ *   page_of      : device int32 [num_seqs][hkv][max_lp]; physical page of each
+ *                  logical page (position / page_size) of this layer, -1 none
+ *   max_rows_per_seq : host bound on cu_rows[b+1]-cu_rows[b] (sizes the grid)
+ * Row r of sequence b, KV head g, goes to page page_of[b][g][p / P], slot
+ * p % P, p = pos0[b] + r - cu_rows[b]; K as one contiguous row of the page,
+ * V into column p % P of the transposed page. Slots not written keep their
+ * contents. A row whose page id is -1, >= num_pages or whose logical page is
+ * >= max_lp, or whose row index is >= num_rows, is skipped.
+ */
+int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new, int64_t num_rows,
+                      const int32_t *cu_rows, const int32_t *pos0, const int32_t *page_of,
+                      int32_t num_seqs, int32_t max_lp, int32_t max_rows_per_seq, void *stream);
+
+/*
+ * SELECTVISIBLESTATE: build one layer's per-(sequence, KV head) segment
+ * tables on the host. All pointers are host memory.
+ *
+ * For segment s = b*hkv + g:
+ *   global head: k_pos0 = 0
+ *   local head:  k_pos0 = floor(max(0, c_b - W + 1) / P) * P, the start of the
+ *                page holding the first key visible to query row 0
+ *   page list  = page_of[b][g][k_pos0/P .. (T_b-1)/P] (every id must be in
+ *                [0, num_pages), else SEGKV_ERR_OUT_OF_RANGE; ids before
+ *                k_pos0/P are not read and may be -1)
+ *   k_len      = T_b - k_pos0
+ *   pairs[s]   = G * sum over new rows i of |visible keys of i|   (int64)
+ * Also emits cu_seqlens_q [S+1], cu_seqlens_k [num_segments+1] (prefix sums
+ * of k_len), cu_pages [num_segments+1], and the attention kernel's work
+ * list: every (segment, row block, head block) once, ordered by descending
+ * cost (KV tiles visited) so that a launch dispatches the longest units
+ * first (longest-processing-time-first balance across heads of very unequal
+ * length).
+ */
+typedef struct segkv_table_inputs {
+    int32_t num_seqs;
+    int32_t max_lp;
+    const int32_t *cached_len;  /* [num_seqs] c_b >= 0 */
+    const int32_t *new_len;     /* [num_seqs] n_b >= 1 */
+    const int8_t *head_class;   /* [hkv] 1 = global, 0 = local (this layer) */
+    const int32_t *window;      /* [hkv] W >= 1 for local heads; ignored for global */
+    const int32_t *page_of;     /* [num_seqs][hkv][max_lp] (this layer) */
+} segkv_table_inputs;
+
+typedef struct segkv_tables {
+    /* capacities of the caller's buffers, in elements (set by the caller) */
+    int32_t seg_cap;            /* segments: >= num_seqs * hkv */
+    int32_t seq_cap;            /* sequences: >= num_seqs */
+    int64_t page_cap;           /* page_list entries */
+    int32_t unit_cap;           /* work units */
+    /* sizes written by the builder (also when it returns SEGKV_ERR_CAPACITY) */
+    int32_t num_segments;
+    int32_t num_units;
+    int64_t num_page_entries;
+    int64_t total_pairs;        /* sum of pairs[] */
+    int32_t total_q_rows;       /* sum of n_b */
+    int32_t unit_rows;          /* query rows per work unit */
+    int32_t unit_heads;         /* query heads per work unit */
+    /* caller-owned host buffers (may be NULL when the matching capacity is 0) */
+    int32_t *seg_desc;          /* [seg_cap][SEGKV_SEG_FIELDS] */
+    int32_t *cu_seqlens_q;      /* [seq_cap + 1] */
+    int32_t *cu_seqlens_k;      /* [seg_cap + 1] */
+    int32_t *cu_pages;          /* [seg_cap + 1] */
+    int32_t *page_list;         /* [page_cap] */
+    int64_t *pairs;             /* [seg_cap] */
+    int32_t *work;              /* [unit_cap][SEGKV_UNIT_FIELDS] */
+} segkv_tables;
+
+int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_inputs *in, segkv_tables *out);
+
+/* Device copies of one layer's tables, as consumed by segkv_attn_prefill. */
+typedef struct segkv_dev_tables {
+    const int32_t *seg_desc;    /* device [num_segments][SEGKV_SEG_FIELDS] */
+    const int32_t *page_list;   /* device [num_page_entries] */
+    const int32_t *work;        /* device [num_units][SEGKV_UNIT_FIELDS] */
+    int32_t num_segments;
+    int32_t num_units;
+    int64_t num_page_entries;
+    int32_t total_q_rows;
+    int32_t unit_rows;          /* must equal the builder's values for this context */
+    int32_t unit_heads;
+} segkv_dev_tables;
+
+/*
+ * EXECUTE: fused variable-length causal prefill attention over every
+ * segment's visible keys, for all query heads, in one launch.
+ *   q   : device bf16 [total_q_rows][hq][head_dim]
+ *   o   : device [total_q_rows][hq][head_dim], fp32 or bf16 per o_dtype
+ *   lse : device fp32 [hq][total_q_rows] natural-log sum of exp of the scaled
+ *         scores, or NULL
+ *   softmax_scale : multiplies q.k; <= 0 selects 1/sqrt(head_dim)
+ * For query row t of segment s and query head h of its group, position
+ * i = q_pos0 + t:  O = sum_j softmax_j(scale * q.k_j) v_j over the visible
+ * keys j of i, computed with bf16 inputs, fp32 accumulation and an online
+ * (running-maximum) softmax. Every output row is written exactly once.
+ */
+int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
+                       int32_t o_dtype, float *lse, float softmax_scale, void *stream);
+
+/*
+ * Read pages back in a dense layout (tests, debugging):
+ *   page_ids : device int32 [n]
+ *   k_out, v_out : device bf16 [n][page_size][head_dim] each (V un-transposed)
+ * An id outside [0, num_pages) yields zeros.
+ */
+int segkv_gather_pages(const segkv_ctx *ctx, const int32_t *page_ids, int64_t n,
+                       void *k_out, void *v_out, void *stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *segkv_last_error(void);
+
+/* Library version string. */
+const char *segkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGKV_H */

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (paged write, host tables, fused attention, all
+through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bar (fp32 output, bf16 inputs, fp32 accumulation): max-abs <= 1e-2 and
+mean-abs <= 1e-3 against the oracle, LSE within 2e-3. The bf16 output mode
+must equal the fp32 output rounded to nearest-even, bit for bit. Page
+tables are bit-exact (tests/test_tables_vs_oracle.py); the paged write is
+bit-exact against the oracle's own scatter. Outputs are bitwise invariant
+under physical page relabelling, reruns and NaN-poisoned free slots.
+
+Small cases run every query; full-size workloads run sampled rows (first
+and last rows, window-edge and page-boundary rows, seeded-uniform rows),
+which the oracle computes one by one.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged as opaged
+from oracle import tables as otables
+from tests.common import adhoc
+from tests.gpu_helpers import GpuLayer, compare, device_pools, host_bits, sample_rows, say
+from workloads import LLAMA70B_32K, MISTRAL_8K, STACK64_128K, TINY, VARLEN_CHUNKED, layer_tensors, realize
+from workloads.gen import relabel_pages
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def oracle_queries(w, r, layer, bits, queries, page_of=None):
+    """Oracle results for (b, h, t) queries of one layer: own tables, own paged write."""
+    po = r.page_of[layer] if page_of is None else page_of
+    tab = otables.build_tables(r.cached_len, r.new_len, r.head_class[layer], r.window[layer], po,
+                               w.hq, w.hkv, w.page, r.num_pages)
+    kp, vp = opaged.empty_pools(r.num_pages, w.page, w.d)
+    opaged.scatter_pages(kp, vp, po, r.cached_len, r.new_len, bits["k_cached"], bits["v_cached"],
+                         bits["k_new"], bits["v_new"])
+    o, lse = opaged.attention(kp, vp, bits["q"], tab, queries)
+    del kp, vp
+    return o, lse, tab
+
+
+def all_queries(w, r):
+    out = []
+    for b in range(r.num_seqs):
+        n = int(r.new_len[b])
+        for h in range(w.hq):
+            out.append(np.stack([np.full(n, b), np.full(n, h), np.arange(n)], 1))
+    return np.concatenate(out).astype(np.int32)
+
+
+def sampled_queries(w, r, layer, seed, n_uniform=256, heads=None):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for b in range(r.num_seqs):
+        c, n = int(r.cached_len[b]), int(r.new_len[b])
+        for h in (range(w.hq) if heads is None else heads):
+            g = h // (w.hq // w.hkv)
+            W = int(r.window[layer][g]) or w.window
+            t = sample_rows(n, c, W, w.page, rng, n_uniform=n_uniform)
+            out.append(np.stack([np.full(len(t), b), np.full(len(t), h), t], 1))
+    return np.concatenate(out).astype(np.int32)
+
+
+def run_case(w, layer=0, queries="all", seed=0, o_dtype=torch.float32, **kw):
+    r = realize(w)
+    say(f"[case] {w.name} layer {layer} hq {w.hq} hkv {w.hkv} D {w.d} P {w.page} "
+        f"seqs {list(zip(r.cached_len.tolist(), r.new_len.tolist()))[:4]}")
+    t = layer_tensors(w, r, layer, device="cuda")
+    gl = GpuLayer(w, r, layer, t, **kw)
+    o, lse = gl.run(o_dtype)
+    bits = {k: host_bits(v) for k, v in t.items()}
+    q = all_queries(w, r) if queries == "all" else sampled_queries(w, r, layer, seed)
+    oo, ol, tab = oracle_queries(w, r, layer, bits, q, page_of=kw.get("page_of"))
+    stats = compare(o, lse, oo, ol, q, tab, w.hkv)
+    say(f"[ok] {w.name} layer {layer}: {stats}")
+    return o, lse, gl
+
+
+def test_tiny_all_rows():
+    o, lse, gl = run_case(TINY)
+    # bf16 output is the fp32 output rounded to nearest even
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+
+
+RAGGED = [
+    # (hq, hkv, d, page, window, classes, seqs)
+    (4, 2, 64, 16, 64, (1, 0), ((0, 333),)),
+    (8, 2, 128, 64, 100, (0, 1), ((0, 200), (37, 301), (1000, 77))),
+    (4, 4, 128, 16, 17, (0, 1, 0, 1), ((5, 130), (64, 64))),
+    (8, 1, 128, 32, 1, (0,), ((0, 97),)),
+    (16, 2, 64, 128, 300, (0, 0), ((250, 260), (0, 1))),
+    (6, 3, 128, 256, 40, (1, 0, 0), ((700, 45), (3, 250))),
+    (2, 2, 64, 64, 2000, (0, 1), ((0, 513),)),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_w{c[4]}")
+def test_ragged_all_rows(case):
+    hq, hkv, d, page, window, classes, seqs = case
+    run_case(adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * d + page))
+
+
+def test_mistral_8k_sampled():
+    run_case(MISTRAL_8K, queries="sampled", seed=2)
+
+
+def test_llama70b_32k_sampled():
+    run_case(LLAMA70B_32K, queries="sampled", seed=3)
+
+
+def test_varlen_chunked_sampled():
+    run_case(VARLEN_CHUNKED, queries="sampled", seed=5)
+
+
+def _stack_layers():
+    r = realize(STACK64_128K)
+    g = r.head_class.sum(axis=1)
+    if os.environ.get("SEGKV_FULL_STACK") == "1":
+        return list(range(STACK64_128K.layers))
+    pick = {0, 7, 8, int(np.argmax(g)), 63}
+    return sorted(pick)
+
+
+def test_stack128k_sampled_layers():
+    w = STACK64_128K
+    r = realize(w)
+    pools = device_pools(r.num_pages, w.page, w.d)
+    for layer in _stack_layers():
+        say(f"[case] {w.name} layer {layer} globals {int(r.head_class[layer].sum())}")
+        t = layer_tensors(w, r, layer, device="cuda")
+        gl = GpuLayer(w, r, layer, t, pools=pools)
+        o, lse = gl.run(torch.float32)
+        bits = {k: host_bits(v) for k, v in t.items()}
+        del t, gl
+        q = sampled_queries(w, r, layer, seed=100 + layer, n_uniform=48)
+        oo, ol, tab = oracle_queries(w, r, layer, bits, q)
+        stats = compare(o, lse, oo, ol, q, tab, w.hkv)
+        say(f"[ok] {w.name} layer {layer}: {stats}")
+        del o, lse, bits
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", [TINY, adhoc(hq=8, hkv=2, d=128, page=64, window=100, classes=(0, 1),
+                                            seqs=((0, 200), (37, 301)), seed=9)], ids=["tiny", "ragged"])
+def test_bitwise_invariances(w):
+    r = realize(w)
+    t = layer_tensors(w, r, 0, device="cuda")
+    base_o, base_l = GpuLayer(w, r, 0, t).run()
+    # rerun
+    o2, l2 = GpuLayer(w, r, 0, t).run()
+    assert torch.equal(base_o, o2) and torch.equal(base_l, l2)
+    # physical page relabelling
+    po = relabel_pages(r.page_of, r.num_pages, 77)[0]
+    o3, l3 = GpuLayer(w, r, 0, t, page_of=po).run()
+    assert torch.equal(base_o, o3) and torch.equal(base_l, l3)
+    # NaN in every slot that is never written (free pages, page tails)
+    o4, l4 = GpuLayer(w, r, 0, t, poison=True).run()
+    assert torch.equal(base_o, o4) and torch.equal(base_l, l4)
+
+
+def test_write_gather_roundtrip_bit_exact():
+    import head_segmented_paged_amd as H
+    w = adhoc(hq=4, hkv=2, d=128, page=16, window=20, classes=(1, 0), seqs=((37, 100), (0, 5), (16, 16)), seed=4)
+    r = realize(w)
+    t = layer_tensors(w, r, 0, device="cuda")
+    gl = GpuLayer(w, r, 0, t, poison=True)
+    gl.write()
+    torch.cuda.synchronize()
+    bits = {k: host_bits(v) for k, v in t.items()}
+    kp, vp = opaged.empty_pools(r.num_pages, w.page, w.d)
+    written = np.zeros(r.num_pages, bool)
+    opaged.scatter_pages(kp, vp, r.page_of[0], r.cached_len, r.new_len, bits["k_cached"], bits["v_cached"],
+                         bits["k_new"], bits["v_new"])
+    ids = np.unique(r.page_of[0][r.page_of[0] >= 0]).astype(np.int32)
+    written[ids] = True
+    dev_ids = torch.from_numpy(ids).cuda()
+    ko = torch.empty((len(ids), w.page, w.d), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    H.segkv_gather_pages(gl.ctx, dev_ids, ko, vo)
+    torch.cuda.synchronize()
+    kg, vg = host_bits(ko), host_bits(vo)
+    # every slot of a sequence's positions matches the oracle's scatter bit for bit
+    for b in range(r.num_seqs):
+        T = int(r.cached_len[b] + r.new_len[b])
+        for g in range(w.hkv):
+            for p in range(T):
+                pid = r.page_of[0][b, g, p // w.page]
+                i = np.searchsorted(ids, pid)
+                assert np.array_equal(kg[i, p % w.page], kp[pid, p % w.page])
+                assert np.array_equal(vg[i, p % w.page], vp[pid, :, p % w.page])
+    # free pages are untouched (still NaN)
+    free = np.nonzero(~written)[0][:64]
+    assert torch.isnan(gl.k_pool[torch.from_numpy(free).cuda()].float()).all()
+    assert torch.isnan(gl.v_pool[torch.from_numpy(free).cuda()].float()).all()

@@ -1,0 +1,103 @@
+"""The library's host table builder (segkv_build_head_tables) against the
+oracle's, bit for bit, on every workload (every layer of the 64-layer stack)
+and on small ragged cases; plus the work list's coverage and order."""
+
+import numpy as np
+import pytest
+
+import head_segmented_paged_amd as H
+from oracle.tables import build_tables
+from tests.common import adhoc
+from workloads import ALL, STACK64_128K, realize
+
+FIELDS = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len",
+          "cu_seqlens_q", "cu_seqlens_k", "cu_pages", "page_list", "pairs")
+
+
+class FakeDev:
+    def __init__(self, p):
+        self.p = p
+
+    def data_ptr(self):
+        return self.p
+
+
+def _ctx(w, num_pages):
+    return H.segkv_create(FakeDev(1 << 20), FakeDev(1 << 21), w.hq, w.hkv, w.d, w.page, num_pages=num_pages)
+
+
+def _compare(w, r, layer, ctx):
+    lib = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[layer], r.window[layer],
+                                    r.page_of[layer])
+    ora = build_tables(r.cached_len, r.new_len, r.head_class[layer], r.window[layer], r.page_of[layer],
+                       w.hq, w.hkv, w.page, r.num_pages)
+    for f in FIELDS:
+        a, b = lib[f], ora[f]
+        assert a.dtype == b.dtype, f
+        np.testing.assert_array_equal(a, b, err_msg=f)
+    np.testing.assert_array_equal(lib["page_off"], ora["cu_pages"][:-1])
+    assert lib["total_pairs"] == int(ora["pairs"].sum())
+    return lib
+
+
+def _check_work(lib, w):
+    G = w.hq // w.hkv
+    work = lib["work"]
+    rows, heads = lib["unit_rows"], lib["unit_heads"]
+    assert rows * heads == 128
+    # longest first
+    assert (np.diff(work[:, 3]) <= 0).all()
+    # every (segment, head, row) exactly once
+    for s in range(lib["num_segments"]):
+        n = lib["n_q"][s]
+        g = lib["kv_head"][s]
+        cnt = np.zeros((G, n), np.int32)
+        mine = work[work[:, 0] == s]
+        for seg, r0, h0, _ in mine:
+            assert g * G <= h0 and h0 + heads <= (g + 1) * G and r0 % rows == 0
+            cnt[h0 - g * G: h0 - g * G + heads, r0: min(r0 + rows, n)] += 1
+        assert (cnt == 1).all()
+    # the cost is the number of 64-key tiles between the first visible key of
+    # the unit's first row and the last row's own key
+    for seg, r0, h0, tiles in work[:: max(1, len(work) // 500)]:
+        c, W, k0 = lib["q_pos0"][seg], lib["window"][seg], lib["k_pos0"][seg]
+        last = c + min(r0 + rows, lib["n_q"][seg]) - 1
+        lo = 0 if W == 0 else max(0, c + r0 - W + 1)
+        assert tiles == -(-(last + 1 - k0) // 64) - (lo - k0) // 64
+
+
+@pytest.mark.parametrize("w", [x for x in ALL if x.layers == 1], ids=lambda w: w.name)
+def test_single_layer_workloads(w):
+    r = realize(w)
+    ctx = _ctx(w, r.num_pages)
+    lib = _compare(w, r, 0, ctx)
+    _check_work(lib, w)
+
+
+def test_stack_all_layers():
+    w = STACK64_128K
+    r = realize(w)
+    ctx = _ctx(w, r.num_pages)
+    for layer in range(w.layers):
+        lib = _compare(w, r, layer, ctx)
+        if layer in (0, 8, 63):
+            work = lib["work"]
+            assert (np.diff(work[:, 3]) <= 0).all()
+            assert len(work) == 8 * (131072 // 32)
+
+
+SMALL = [((0, 1),), ((0, 17),), ((5, 30),), ((37, 100),), ((0, 100), (37, 15), (5, 2)),
+         ((16, 16), (15, 1)), ((100, 20),), ((64, 64),), ((3, 13), (0, 50), (200, 33))]
+
+
+@pytest.mark.parametrize("seqs", SMALL)
+@pytest.mark.parametrize("W", [1, 16, 17, 64])
+@pytest.mark.parametrize("shape", [(4, 2, (1, 0)), (8, 2, (0, 1)), (3, 3, (0, 1, 1)), (8, 1, (0,))])
+@pytest.mark.parametrize("page", [16, 64])
+def test_small_cases(seqs, W, shape, page):
+    hq, hkv, classes = shape
+    w = adhoc(hq=hq, hkv=hkv, d=64, page=page, window=W, classes=classes, seqs=seqs, seed=W + page)
+    r = realize(w)
+    ctx = _ctx(w, r.num_pages)
+    lib = _compare(w, r, 0, ctx)
+    _check_work(lib, w)
