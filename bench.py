@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""SegPaged prefill benchmark on one MI355X.
+
+One step is one pass of the whole hot path over the 64-layer 128K stack
+(32 query / 8 KV heads, head dim 128, page 64, window 2048; each (layer, KV
+head) global with probability 0.13, layers 0-7 all local):
+  * per layer, the host builds the head-class page tables and work list
+    (segkv_build_head_tables) and uploads them asynchronously;
+  * the layer's new K/V rows are written into their pages (segkv_write_pages);
+  * the fused varlen attention runs over every head's visible keys
+    (segkv_attn_prefill, bf16 output).
+Layers run one after another on one stream, as a real prefill would. All
+inputs (Q, K, V for every layer, the block tables, the pools) are resident in
+HBM before the timed region.
+
+The headline value is useful TFLOP/s: 4 * head_dim FLOPs per visible
+(query, key) pair per query head, over the step time. The roofline object
+reports the attention kernel alone against the bf16 MFMA peak, timed with HIP
+events on the launch stream. A bounded sample of the fp64 CPU oracle runs
+beside it on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "SegPagedAttention prefill TFLOP/s + ms/layer at 32K/128K; % bf16 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class LayerTables:
+    """One layer's tables: rebuilt on the host each step, uploaded through
+    pinned buffers on the launch stream."""
+
+    def __init__(self, H, S, torch, ctx, r, layer, device):
+        self.H, self.torch, self.ctx = H, torch, ctx
+        self.args = (r.cached_len, r.new_len, r.head_class[layer], r.window[layer], r.page_of[layer])
+        host = H.segkv_build_head_tables(ctx, *self.args)
+        self.keys = ("seg_desc", "page_list", "work")
+        self.pin = {k: torch.empty(host[k].shape, dtype=torch.int32, pin_memory=True) for k in self.keys}
+        self.dev = {k: torch.empty(host[k].shape, dtype=torch.int32, device=device) for k in self.keys}
+        self.pairs = host["total_pairs"]
+        self.struct = S.segkv_dev_tables(
+            self.dev["seg_desc"].data_ptr(), self.dev["page_list"].data_ptr(), self.dev["work"].data_ptr(),
+            host["num_segments"], host["num_units"], host["num_page_entries"], host["total_q_rows"],
+            host["unit_rows"], host["unit_heads"])
+        self.free = torch.cuda.Event()
+        self.free.record()
+
+    def refresh(self):
+        self.free.synchronize()            # the previous upload from the pinned buffers is done
+        host = self.H.segkv_build_head_tables(self.ctx, *self.args)
+        for k in self.keys:
+            self.pin[k].numpy()[...] = host[k]
+            self.dev[k].copy_(self.pin[k], non_blocking=True)
+        self.free.record()
+        self.pairs = host["total_pairs"]
+
+
+class Resident:
+    """A workload with every layer's inputs resident on the GPU."""
+
+    def __init__(self, w, device="cuda", o_dtype="bf16"):
+        import torch
+        import head_segmented_paged_amd as H
+        from head_segmented_paged_amd import segkv as S
+        from workloads import layer_tensors, prefix, realize
+        self.torch, self.H, self.w = torch, H, w
+        r = self.r = realize(w)
+        t0 = time.perf_counter()
+        self.k_pool = torch.zeros((r.num_pages, w.page, w.d), dtype=torch.bfloat16, device=device)
+        self.v_pool = torch.zeros((r.num_pages, w.d, w.page), dtype=torch.bfloat16, device=device)
+        self.ctx = H.segkv_create(self.k_pool, self.v_pool, w.hq, w.hkv, w.d, w.page)
+        self.page_of = torch.from_numpy(np.ascontiguousarray(r.page_of)).to(device)
+        self.cu_new = torch.from_numpy(prefix(r.new_len)).to(device)
+        self.pos0 = torch.from_numpy(np.ascontiguousarray(r.cached_len, dtype=np.int32)).to(device)
+        self.layers = []
+        for layer in range(w.layers):
+            t = layer_tensors(w, r, layer, device=device)
+            if int(r.cached_len.sum()) > 0:      # the reused cache exists before the request
+                cu_c = torch.from_numpy(prefix(r.cached_len)).to(device)
+                zeros = torch.zeros_like(self.pos0)
+                H.segkv_write_pages(self.ctx, t["k_cached"], t["v_cached"], cu_c, zeros, self.page_of[layer],
+                                    int(r.cached_len.max()))
+            self.layers.append({"q": t["q"], "k_new": t["k_new"], "v_new": t["v_new"]})
+            del t
+        rows = int(r.new_len.sum())
+        odt = torch.bfloat16 if o_dtype == "bf16" else torch.float32
+        self.o = torch.empty((rows, w.hq, w.d), dtype=odt, device=device)
+        self.tables = [LayerTables(H, S, torch, self.ctx, r, layer, device) for layer in range(w.layers)]
+        torch.cuda.synchronize()
+        self.setup_s = time.perf_counter() - t0
+        self.pairs_per_step = sum(int(lt.pairs) for lt in self.tables)
+        self.flops_per_step = 4.0 * w.d * self.pairs_per_step
+
+    def step(self, events=None):
+        H, r = self.H, self.r
+        max_new = int(r.new_len.max())
+        for layer, lt in enumerate(self.tables):
+            lt.refresh()
+            x = self.layers[layer]
+            if events is not None:
+                events[layer][0].record()
+            H.segkv_write_pages(self.ctx, x["k_new"], x["v_new"], self.cu_new, self.pos0, self.page_of[layer],
+                                max_new)
+            if events is not None:
+                events[layer][1].record()
+            H.segkv_attn_prefill(self.ctx, lt, x["q"], self.o)
+            if events is not None:
+                events[layer][2].record()
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in self.tables]
+               for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(evs[s])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        attn = np.array([[e[1].elapsed_time(e[2]) for e in st] for st in evs])    # ms [steps][layers]
+        write = np.array([[e[0].elapsed_time(e[1]) for e in st] for st in evs])
+        return wall, attn, write
+
+
+def cpu_baseline(res, target_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of one layer's queries."""
+    from oracle import paged as opaged
+    from oracle import tables as otables
+    torch, w, r = res.torch, res.w, res.r
+    layer = int(np.argmax(r.head_class.sum(axis=1)))
+    from workloads import layer_tensors
+    t = layer_tensors(w, r, layer, device="cuda")
+    bits = {k: opaged.bf16_bits(v) for k, v in t.items()}
+    del t
+    tab = otables.build_tables(r.cached_len, r.new_len, r.head_class[layer], r.window[layer], r.page_of[layer],
+                               w.hq, w.hkv, w.page, r.num_pages)
+    kp, vp = opaged.empty_pools(r.num_pages, w.page, w.d)
+    opaged.scatter_pages(kp, vp, r.page_of[layer], r.cached_len, r.new_len, bits["k_cached"], bits["v_cached"],
+                         bits["k_new"], bits["v_new"])
+    rng = np.random.Generator(np.random.PCG64(2024))
+    G = w.hq // w.hkv
+
+    def sample(per_head):
+        qs = []
+        for b in range(r.num_seqs):
+            n = int(r.new_len[b])
+            for h in range(w.hq):
+                tt = rng.integers(0, n, size=per_head)
+                qs.append(np.stack([np.full(per_head, b), np.full(per_head, h), tt], 1))
+        q = np.concatenate(qs).astype(np.int32)
+        c = r.cached_len[q[:, 0]].astype(np.int64)
+        win = r.window[layer][q[:, 1] // G].astype(np.int64)
+        i = c + q[:, 2]
+        cnt = np.where(win == 0, i + 1, np.minimum(i + 1, np.maximum(win, 1)))
+        return q, int(cnt.sum())
+
+    q, pairs = sample(4)
+    t0 = time.perf_counter()
+    opaged.attention(kp, vp, bits["q"], tab, q)
+    dt = time.perf_counter() - t0
+    per_head = int(max(4, min(4096, 4 * target_s / max(dt, 1e-3))))
+    q, pairs = sample(per_head)
+    t0 = time.perf_counter()
+    opaged.attention(kp, vp, bits["q"], tab, q)
+    dt = time.perf_counter() - t0
+    del kp, vp
+    return {
+        "value": 4.0 * w.d * pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": opaged.threads(),
+        "kind": "oracle",
+        "sample": (f"{len(q)} queries ({per_head} uniform rows per query head, all {w.hq} heads) of layer {layer} "
+                   f"of {w.name}; {pairs} visible pairs in {dt:.1f} s; fp64"),
+        "ns_per_pair": dt / pairs * 1e9,
+        "extrapolated_step_s": dt / pairs * res.pairs_per_step,
+    }
+
+
+def run_secondary(name, steps=5, warmup=2):
+    from workloads import BY_NAME
+    res = Resident(BY_NAME[name])
+    wall, attn, write = res.timed(steps, warmup)
+    a = float(np.median(attn.sum(axis=1)))
+    out = {
+        "workload": name,
+        "ms_per_layer": a,
+        "tflops": res.flops_per_step / (a / 1e3) / 1e12,
+        "step_ms": wall * 1e3,
+        "write_ms": float(np.median(write.sum(axis=1))),
+    }
+    out["pct_bf16_peak"] = 100.0 * out["tflops"] / PEAK_BF16_TFLOPS
+    del res
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="stack64_l131072")
+    ap.add_argument("--o-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import BY_NAME
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = BY_NAME[args.workload]
+    log(f"[bench] setting up {w.name} ({w.layers} layers)")
+    res = Resident(w, o_dtype=args.o_dtype)
+    log(f"[bench] setup {res.setup_s:.1f} s; running {args.warmup} warmup + {args.steps} timed steps")
+    wall, attn, write = res.timed(args.steps, args.warmup)
+    attn_step = attn.sum(axis=1)                      # ms per step, attention launches only
+    write_step = write.sum(axis=1)
+    achieved = res.flops_per_step / (float(np.mean(attn_step)) / 1e3) / 1e12
+    value = res.flops_per_step / wall / 1e12
+    r = res.r
+    globals_per_layer = r.head_class.sum(axis=1).tolist()
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": w.layers, "seq_len": int(r.cached_len[0] + r.new_len[0]),
+            "num_seqs": r.num_seqs, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "page_size": w.page,
+            "window": w.window, "global_kv_heads": int(sum(globals_per_layer)),
+            "kv_heads_total": w.layers * w.hkv, "o_dtype": args.o_dtype,
+        },
+        "ms_per_layer": float(np.mean(attn_step)) / w.layers,
+        "ms_per_layer_step": wall * 1e3 / w.layers,
+        "attn_ms_total": float(np.mean(attn_step)),
+        "write_ms_total": float(np.mean(write_step)),
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "visible_pairs_per_step": res.pairs_per_step,
+        "useful_flops_per_step": res.flops_per_step,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+        "globals_per_layer": globals_per_layer,
+    }
+    if not args.no_secondary and w.name == "stack64_l131072":
+        del res
+        torch.cuda.empty_cache()
+        log("[bench] secondary: llama70b_like_l32768")
+        line["at_32k"] = run_secondary("llama70b_like_l32768")
+        res = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle sample)")
+        if res is None:
+            res = Resident(w, o_dtype=args.o_dtype) if w.layers == 1 else _light(w)
+        line["cpu_baseline"] = cpu_baseline(res)
+    print(json.dumps(line), flush=True)
+
+
+class _Light:
+    pass
+
+
+def _light(w):
+    """Metadata-only stand-in for the CPU baseline (no GPU buffers)."""
+    import torch
+    from workloads import realize
+    x = _Light()
+    x.torch, x.w, x.r = torch, w, realize(w)
+    from oracle import tables as otables
+    x.pairs_per_step = 0
+    for layer in range(w.layers):
+        t = otables.build_tables(x.r.cached_len, x.r.new_len, x.r.head_class[layer], x.r.window[layer],
+                                 x.r.page_of[layer], w.hq, w.hkv, w.page, x.r.num_pages)
+        x.pairs_per_step += int(t["pairs"].sum())
+    return x
+
+
+if __name__ == "__main__":
+    main()

@@ -65,62 +65,82 @@ template <int D>
 struct Staged {
     u32x4 k[Tile<D>::kPerThread];
     u32x4 v[Tile<D>::vPerThread];
+    unsigned ok;  // bit r: K chunk r usable; bit 8 + r: V chunk r has a usable page
 };
 
 // K row fed to MFMA row r: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int swizzle_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Fetch one KV tile (keys tile_key0 .. tile_key0+63 of the segment) from the
-// pools into registers. Keys outside [zero_lo, zero_hi) become zeros.
-template <int D>
+// Physical page holding logical page lp of the segment, or -1.
+__device__ __forceinline__ int page_id(const int32_t *__restrict__ pages, int n_pages, int64_t num_pages, int lp)
+{
+    const int id = pages[min(max(lp, 0), n_pages - 1)];
+    return (lp >= 0 && lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+}
+
+// Issue the loads of one KV tile (keys tile_key0 .. tile_key0+63 of the
+// segment) into registers. Every lane loads from a valid address; whether a
+// chunk may be used is recorded in st.ok and applied when the tile is
+// written to LDS, so the loads of a tile are all in flight together and
+// nothing waits on them here.
+//   BIG_PAGE (P >= 64): the tile lies inside one page whose id `tile_page`
+//   the caller loaded ahead of time (workgroup-uniform).
+//   otherwise: the tile spans 64 / P pages; each lane looks up its chunks'
+//   ids first (all id loads together), then issues its data loads.
+template <int D, bool BIG_PAGE>
 __device__ __forceinline__ void fetch_tile(Staged<D> &st, const u16 *__restrict__ kpool,
                                            const u16 *__restrict__ vpool, const int32_t *__restrict__ pages,
                                            int32_t n_pages, int64_t num_pages, int log2P, int tile_key0,
-                                           int zero_lo, int zero_hi)
+                                           int tile_page, int zero_lo, int zero_hi)
 {
     const int pmask = (1 << log2P) - 1;
+    int kpage[Tile<D>::kPerThread], vpage[Tile<D>::vPerThread];
+    if constexpr (BIG_PAGE) {
+#pragma unroll
+        for (int r = 0; r < Tile<D>::kPerThread; ++r) kpage[r] = tile_page;
+#pragma unroll
+        for (int r = 0; r < Tile<D>::vPerThread; ++r) vpage[r] = tile_page;
+    } else {
+#pragma unroll
+        for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+            const int c = threadIdx.x + r * kThreads;
+            kpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + c / (D / 8)) >> log2P);
+        }
+#pragma unroll
+        for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+            const int c = threadIdx.x + r * kThreads;
+            vpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + (c % (kBK / 8)) * 8) >> log2P);
+        }
+    }
+    unsigned ok = 0;
 #pragma unroll
     for (int r = 0; r < Tile<D>::kPerThread; ++r) {
         const int c = threadIdx.x + r * kThreads;
         const int key = c / (D / 8), dc = c % (D / 8);
         const int idx = tile_key0 + key;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (idx >= 0 && idx >= zero_lo && idx < zero_hi) {
-            const int lpi = idx >> log2P;
-            const int page = lpi < n_pages ? pages[lpi] : -1;
-            if (page >= 0 && page < num_pages)
-                val = *reinterpret_cast<const u32x4 *>(
-                    kpool + ((static_cast<int64_t>(page) << log2P) + (idx & pmask)) * D + dc * 8);
-        }
-        st.k[r] = val;
+        const bool use = idx >= zero_lo && idx < zero_hi && kpage[r] >= 0;
+        const int64_t pg = use ? kpage[r] : 0;
+        ok |= use ? (1u << r) : 0u;
+        st.k[r] = *reinterpret_cast<const u32x4 *>(kpool + ((pg << log2P) + (idx & pmask)) * D + dc * 8);
     }
 #pragma unroll
     for (int r = 0; r < Tile<D>::vPerThread; ++r) {
         const int c = threadIdx.x + r * kThreads;
         const int d = c / (kBK / 8), kc = c % (kBK / 8);
         const int idx0 = tile_key0 + kc * 8;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (idx0 >= 0 && idx0 + 7 >= zero_lo && idx0 < zero_hi) {
-            const int lpi = idx0 >> log2P;
-            const int page = lpi < n_pages ? pages[lpi] : -1;
-            if (page >= 0 && page < num_pages) {
-                val = *reinterpret_cast<const u32x4 *>(
-                    vpool + ((static_cast<int64_t>(page) * D + d) << log2P) + (idx0 & pmask));
-                if (idx0 < zero_lo || idx0 + 8 > zero_hi) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int idx = idx0 + i;
-                        if (idx < zero_lo || idx >= zero_hi) val[i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
-                    }
-                }
-            }
-        }
-        st.v[r] = val;
+        const bool use = idx0 + 7 >= zero_lo && idx0 < zero_hi && vpage[r] >= 0;
+        const int64_t pg = use ? vpage[r] : 0;
+        ok |= use ? (1u << (8 + r)) : 0u;
+        st.v[r] = *reinterpret_cast<const u32x4 *>(vpool + ((pg * D + d) << log2P) + (idx0 & pmask));
     }
+    st.ok = ok;
 }
 
+// Write a fetched tile to one LDS stage, zeroing what must not be used
+// (keys outside [zero_lo, zero_hi) or on a missing page).
 template <int D>
-__device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict__ stage)
+__device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict__ stage, int tile_key0,
+                                           int zero_lo, int zero_hi)
 {
     u16 *ks = stage;
     u16 *vs = stage + Tile<D>::kElems;
@@ -128,17 +148,27 @@ __device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict_
     for (int r = 0; r < Tile<D>::kPerThread; ++r) {
         const int c = threadIdx.x + r * kThreads;
         const int key = c / (D / 8), dc = c % (D / 8);
-        *reinterpret_cast<u32x4 *>(ks + key * Tile<D>::kLd + dc * 8) = st.k[r];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(ks + key * Tile<D>::kLd + dc * 8) = (st.ok >> r) & 1u ? st.k[r] : z;
     }
 #pragma unroll
     for (int r = 0; r < Tile<D>::vPerThread; ++r) {
         const int c = threadIdx.x + r * kThreads;
         const int d = c / (kBK / 8), kc = c % (kBK / 8);
-        *reinterpret_cast<u32x4 *>(vs + d * Tile<D>::vLd + kc * 8) = st.v[r];
+        const int idx0 = tile_key0 + kc * 8;
+        u32x4 val = (st.ok >> (8 + r)) & 1u ? st.v[r] : u32x4{0u, 0u, 0u, 0u};
+        if (idx0 < zero_lo || idx0 + 8 > zero_hi) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int idx = idx0 + i;
+                if (idx < zero_lo || idx >= zero_hi) val[i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+        }
+        *reinterpret_cast<u32x4 *>(vs + d * Tile<D>::vLd + kc * 8) = val;
     }
 }
 
-template <int D, int HPW, bool OUT_BF16>
+template <int D, int HPW, bool OUT_BF16, bool BIG_PAGE>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
     const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
     const int page_off = desc[SEGKV_SEG_PAGE_OFF];
-    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off > num_page_entries) return;
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
     int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
     if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
     const int32_t *pages = page_list + page_off;
@@ -176,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const int tile_beg = (lo_pos - k_pos0) / kBK;
     const int tile_end = (last_pos + 1 - k_pos0 + kBK - 1) / kBK;
     // Stored keys that some query of the segment can see; everything else is zero-filled.
-    const int zero_lo = (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0;
+    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
     const int zero_hi = k_len;
 
     // This wavefront's rows.
@@ -185,6 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const int wp_lo = q_pos0 + wrow0, wp_hi = q_pos0 + wrow_end - 1;
     const int my_t = min(wrow0 + col, n_q - 1);
     const int my_pos = q_pos0 + my_t;
+    const int lo_i = window ? my_pos - window + 1 : -(1 << 30);   // first visible key position of this lane's row
     const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
     const bool row_ok = wave_valid && (wrow0 + col) < n_q && my_row < total_q_rows;
 
@@ -205,16 +236,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
     float m = kNegBig, lsum = 0.f;
 
+    // Tile jt covers keys [64 jt, 64 jt + 64) of the segment. With BIG_PAGE it
+    // lies in logical page (64 jt) >> log2P. Page ids are read 64 at a time,
+    // one per lane, into a register window (the next window is loaded while the
+    // current one is in use), and a tile's id is taken from it with a lane read.
+    const int lp_first = (tile_beg * kBK) >> log2P;
+    int win = lp_first >> 6;
+    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
+    int win_cur = 0, win_next = 0;
+    if constexpr (BIG_PAGE) {
+        win_cur = load_window(win);
+        win_next = load_window(win + 1);
+    }
+    auto tile_page = [&](int jt) {
+        if constexpr (!BIG_PAGE) return 0;
+        const int lp = (jt * kBK) >> log2P;
+        if ((lp >> 6) != win) {  // tiles advance in order: step to the prefetched window
+            win = lp >> 6;
+            win_cur = win_next;
+            win_next = load_window(win + 1);
+        }
+        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
+        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    };
     Staged<D> st;
-    fetch_tile<D>(st, kpool, vpool, pages, n_pages, num_pages, log2P, tile_beg * kBK, zero_lo, zero_hi);
-    store_tile<D>(st, smem);
+    fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, tile_beg * kBK, tile_page(tile_beg),
+                            zero_lo, zero_hi);
+    store_tile<D>(st, smem, tile_beg * kBK, zero_lo, zero_hi);
     __syncthreads();
 
     for (int jt = tile_beg; jt < tile_end; ++jt) {
         const int cur = (jt - tile_beg) & 1;
         const bool more = jt + 1 < tile_end;
         if (more)
-            fetch_tile<D>(st, kpool, vpool, pages, n_pages, num_pages, log2P, (jt + 1) * kBK, zero_lo, zero_hi);
+            fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, (jt + 1) * kBK,
+                                    tile_page(jt + 1), zero_lo, zero_hi);
 
         const u16 *ks = smem + cur * T::stage;
         const u16 *vs = ks + T::kElems;
@@ -235,14 +291,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
                 }
             }
             if (!full) {
+                // key position of accumulator element e of block kb = kbase + const;
+                // visible iff lo_i <= position <= my_pos, one unsigned range test each
+                const int kbase = kp0 + 8 * half;
+                const unsigned span = static_cast<unsigned>(my_pos - lo_i);
+                const int off = kbase - lo_i;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int jj = e >> 2, ii = e & 3;
-                        const int kpos = kp0 + 32 * kb + 16 * (jj >> 1) + 8 * half + 4 * (jj & 1) + ii;
-                        const bool vis = kpos <= my_pos && (window == 0 || my_pos - kpos < window);
-                        if (!vis) sacc[kb][e] = -__builtin_inff();
+                        const int kc = 32 * kb + 16 * (jj >> 1) + 4 * (jj & 1) + ii;
+                        const bool vis = static_cast<unsigned>(off + kc) <= span;
+                        sacc[kb][e] = vis ? sacc[kb][e] : -__builtin_inff();
                     }
             }
             // Running maximum (log2 domain), refreshed only when it grows by more than the slack.
@@ -281,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
                 }
             }
         }
-        if (more) store_tile<D>(st, smem + (cur ^ 1) * T::stage);
+        if (more) store_tile<D>(st, smem + (cur ^ 1) * T::stage, (jt + 1) * kBK, zero_lo, zero_hi);
         __syncthreads();
     }
 
@@ -322,7 +383,9 @@ template <int D, int HPW, bool OUT_BF16>
 void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
             hipStream_t stream)
 {
-    hipLaunchKernelGGL((attn_prefill_kernel<D, HPW, OUT_BF16>), dim3(static_cast<unsigned>(t.num_units)),
+    auto kernel = cfg.page_size >= kBK ? attn_prefill_kernel<D, HPW, OUT_BF16, true>
+                                       : attn_prefill_kernel<D, HPW, OUT_BF16, false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(t.num_units)),
                        dim3(kThreads), 0, stream, static_cast<const u16 *>(q), static_cast<const u16 *>(cfg.k_pool),
                        static_cast<const u16 *>(cfg.v_pool), cfg.num_pages, log2_of(cfg.page_size), t.seg_desc,
                        t.page_list, t.num_page_entries, t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads,

@@ -52,8 +52,14 @@ def load(path=_LIB):
                    P, P, P, P, P, P, P, P, ctypes.c_int64,
                    P, ctypes.c_int64, ctypes.c_double, P, P]
     fn.restype = ctypes.c_int
+    lib.oracle_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
+
+
+def threads(lib_path=_LIB):
+    """OpenMP threads the oracle runs on."""
+    return int(load(lib_path).oracle_threads())
 
 
 def bf16_bits(x) -> np.ndarray:
