@@ -71,6 +71,33 @@ struct Staged {
 // K row fed to MFMA row r: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int swizzle_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Lanes l and l ^ 32 exchange x through v_permlane32_swap (upper half of the
+// first operand <-> lower half of the second). The second operand is a copy
+// the compiler cannot see through: with two operands it can prove equal it
+// folds the swap's second result into the first.
+__device__ __forceinline__ void swap_halves(float x, float &a, float &b)
+{
+    unsigned u = __builtin_bit_cast(unsigned, x), v = u;
+    asm volatile("" : "+v"(v));
+    const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+}
+
+__device__ __forceinline__ float max_halves(float x)
+{
+    float a, b;
+    swap_halves(x, a, b);
+    return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float sum_halves(float x)
+{
+    float a, b;
+    swap_halves(x, a, b);
+    return a + b;
+}
+
 // Physical page holding logical page lp of the segment, or -1.
 __device__ __forceinline__ int page_id(const int32_t *__restrict__ pages, int n_pages, int64_t num_pages, int lp)
 {
@@ -168,6 +195,65 @@ __device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict_
     }
 }
 
+// Fast path for a clean tile (page size >= 64, page present, every key of
+// the tile stored and visible to some query): each thread's chunks sit at
+// fixed byte offsets from a workgroup-uniform base, so a load is one
+// "SGPR base + VGPR offset" instruction and the LDS store needs no masking.
+template <int D>
+struct ChunkOffsets {
+    unsigned k[Tile<D>::kPerThread];  // bytes from the tile's first key in its K page
+    unsigned v[Tile<D>::vPerThread];  // bytes from the tile's first slot in its V page
+};
+
+template <int D>
+__device__ __forceinline__ ChunkOffsets<D> chunk_offsets(int log2P)
+{
+    ChunkOffsets<D> off;
+#pragma unroll
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        off.k[r] = static_cast<unsigned>(((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
+    }
+#pragma unroll
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        off.v[r] = static_cast<unsigned>((((c / (kBK / 8)) << log2P) + (c % (kBK / 8)) * 8) * 2);
+    }
+    return off;
+}
+
+template <int D>
+__device__ __forceinline__ void fetch_clean(Staged<D> &st, const u16 *__restrict__ kpool,
+                                            const u16 *__restrict__ vpool, int log2P, int page, int slot0,
+                                            const ChunkOffsets<D> &off)
+{
+    const char *kb = reinterpret_cast<const char *>(kpool) +
+                     ((static_cast<int64_t>(page) << log2P) + slot0) * static_cast<int64_t>(D * 2);
+    const char *vb = reinterpret_cast<const char *>(vpool) +
+                     (((static_cast<int64_t>(page) * D) << log2P) + slot0) * 2;
+#pragma unroll
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) st.k[r] = *reinterpret_cast<const u32x4 *>(kb + off.k[r]);
+#pragma unroll
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) st.v[r] = *reinterpret_cast<const u32x4 *>(vb + off.v[r]);
+}
+
+template <int D>
+__device__ __forceinline__ void store_clean(const Staged<D> &st, u16 *__restrict__ stage)
+{
+    u16 *ks = stage;
+    u16 *vs = stage + Tile<D>::kElems;
+#pragma unroll
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        *reinterpret_cast<u32x4 *>(ks + (c / (D / 8)) * Tile<D>::kLd + (c % (D / 8)) * 8) = st.k[r];
+    }
+#pragma unroll
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        *reinterpret_cast<u32x4 *>(vs + (c / (kBK / 8)) * Tile<D>::vLd + (c % (kBK / 8)) * 8) = st.v[r];
+    }
+}
+
 template <int D, int HPW, bool OUT_BF16, bool BIG_PAGE>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
@@ -259,18 +345,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
         const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
         return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
     };
+    const ChunkOffsets<D> coff = chunk_offsets<D>(log2P);
+    // Fetch tile jt into st; returns whether it took the clean path.
+    auto fetch = [&](Staged<D> &st, int jt) {
+        const int page = tile_page(jt);
+        const int key0 = jt * kBK;
+        const bool clean = BIG_PAGE && page >= 0 && key0 >= zero_lo && key0 + kBK <= zero_hi;
+        if (clean)
+            fetch_clean<D>(st, kpool, vpool, log2P, page, (k_pos0 + key0) & ((1 << log2P) - 1), coff);
+        else
+            fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, key0, page, zero_lo,
+                                    zero_hi);
+        return clean;
+    };
+    auto store = [&](const Staged<D> &st, bool clean, u16 *stage, int jt) {
+        if (clean)
+            store_clean<D>(st, stage);
+        else
+            store_tile<D>(st, stage, jt * kBK, zero_lo, zero_hi);
+    };
     Staged<D> st;
-    fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, tile_beg * kBK, tile_page(tile_beg),
-                            zero_lo, zero_hi);
-    store_tile<D>(st, smem, tile_beg * kBK, zero_lo, zero_hi);
+    store(st, fetch(st, tile_beg), smem, tile_beg);
     __syncthreads();
 
     for (int jt = tile_beg; jt < tile_end; ++jt) {
         const int cur = (jt - tile_beg) & 1;
         const bool more = jt + 1 < tile_end;
-        if (more)
-            fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, (jt + 1) * kBK,
-                                    tile_page(jt + 1), zero_lo, zero_hi);
+        bool clean_next = false;
+        if (more) clean_next = fetch(st, jt + 1);
 
         const u16 *ks = smem + cur * T::stage;
         const u16 *vs = ks + T::kElems;
@@ -312,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+            mt = max_halves(mt) * scale_log2;
             if (__any(mt > m + kRescaleSlack)) {
                 const float m_new = fmaxf(m, mt);
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -342,12 +444,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
                 }
             }
         }
-        if (more) store_tile<D>(st, smem + (cur ^ 1) * T::stage, (jt + 1) * kBK, zero_lo, zero_hi);
+        if (more) store(st, clean_next, smem + (cur ^ 1) * T::stage, jt + 1);
         __syncthreads();
     }
 
     // Epilogue: combine the two halves' row sums, normalise, store.
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = sum_halves(lsum);
     if (!row_ok) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     const int64_t obase = (my_row * hq + head) * D;
