@@ -1,6 +1,8 @@
 """Build libsegkv.so (HIP kernels for gfx950 + host C++) in-tree.
 
-    python -m head_segmented_paged_amd.build
+    python head_segmented_paged_amd/build.py [--isa]
+
+(Run it by path: importing the package loads the library being rebuilt.)
 
 HIP sources go through hipcc for gfx950 only; host-only C++ goes through g++.
 Every HIP compile carries `-Xclang -target-feature -Xclang -packed-fp32-ops`

@@ -474,6 +474,317 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
         lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
+// ---------------------------------------------------------------------------
+// Page size >= 64. A KV tile then lies inside one page, and its K and V^T
+// rows are copied straight from the pools into LDS by the load unit
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane),
+// so no VGPRs hold a tile in flight and those registers go to a deeper LDS
+// operand prefetch instead. Because a DMA writes 1 KiB contiguously per
+// wave instruction, tile rows are unpadded; an XOR swizzle of the 16-byte
+// chunk position keeps the MFMA operand reads free of bank conflicts. The
+// two LDS stages are separate arrays so the compiler can see that reading
+// one never waits for the DMA into the other.
+template <int D>
+struct DmaTile {
+    static constexpr int kRowBytes = D * 2;                   // one key of K
+    static constexpr int kBytes = kBK * kRowBytes;            // K tile
+    static constexpr int vBytes = D * kBK * 2;                // V^T tile: D rows of 64 keys
+    static constexpr int bytes = kBytes + vBytes;
+    static constexpr int kInstr = kBytes / 1024 / kWaves;     // DMA instructions per wave
+    static constexpr int vInstr = vBytes / 1024 / kWaves;
+};
+// Chunk swizzles: K row r keeps logical chunk c at position c ^ kswz(r); V^T
+// row d keeps key chunk c at position c ^ vswz(d).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer resource straight into LDS at lds + 16 * lane.
+// (A device function: the builtin must not appear in the kernel body itself,
+// where the host pass would drop the kernel's launch stub.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char *lds, unsigned voffset, unsigned soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds, 16, voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const u16 *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16 *>(base), 0, bytes, 0x00020000);
+}
+
+template <int D, int HPW, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
+    int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
+    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
+    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse)
+{
+    using T = DmaTile<D>;
+    constexpr int kRowBlocks = kWaves / HPW;
+    constexpr int kUnitRows = kWaveRows * kRowBlocks;
+    constexpr int kSteps = D / 16;      // MFMA k-steps over the head dim for S^T
+    constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(1024))) char stage0[T::bytes];
+    __shared__ __attribute__((aligned(1024))) char stage1[T::bytes];
+
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS);
+    const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
+    if (seg < 0 || seg >= num_segments) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
+    int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
+    if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
+    const int32_t *pages = page_list + page_off;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const int head = head0 + wave % HPW;
+    const int wrow0 = row0 + (wave / HPW) * kWaveRows;
+
+    const int unit_end = min(row0 + kUnitRows, n_q);
+    const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
+    const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
+    const int tile_beg = (lo_pos - k_pos0) / kBK;
+    const int tile_end = (last_pos + 1 - k_pos0 + kBK - 1) / kBK;
+    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
+    const int zero_hi = k_len;
+
+    const bool wave_valid = wrow0 < n_q && head < hq;
+    const int wrow_end = min(wrow0 + kWaveRows, n_q);
+    const int wp_lo = q_pos0 + wrow0, wp_hi = q_pos0 + wrow_end - 1;
+    const int my_t = min(wrow0 + col, n_q - 1);
+    const int my_pos = q_pos0 + my_t;
+    const int lo_i = window ? my_pos - window + 1 : -(1 << 30);
+    const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
+    const bool row_ok = wave_valid && (wrow0 + col) < n_q && my_row < total_q_rows;
+
+    bf16x8 qreg[kSteps];
+    {
+        const bool can_load = wave_valid && my_row < total_q_rows;
+        const u16 *qp = q + (my_row * hq + head) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+            qreg[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    f32x16 oacc[kDBlocks];
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
+    float m = kNegBig, lsum = 0.f;
+
+    // Page ids: a 64-entry register window per wave, read with v_readlane.
+    int win = ((tile_beg * kBK) >> log2P) >> 6;
+    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
+    int win_cur = load_window(win), win_next = load_window(win + 1);
+    auto tile_page = [&](int jt) {
+        const int lp = (jt * kBK) >> log2P;
+        if ((lp >> 6) != win) {
+            win = lp >> 6;
+            win_cur = win_next;
+            win_next = load_window(win + 1);
+        }
+        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
+        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    };
+
+    // Per-lane DMA source offsets (bytes from the tile's first key in its page).
+    unsigned kdma[T::kInstr], vdma[T::vInstr];
+#pragma unroll
+    for (int i = 0; i < T::kInstr; ++i) {
+        const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
+        const int r = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(r);
+        kdma[i] = static_cast<unsigned>(r * T::kRowBytes + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < T::vInstr; ++i) {
+        const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
+        const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
+        vdma[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
+    }
+    // One buffer resource per page: an out-of-range offset, or a missing page
+    // (zero records), reads as zeros.
+    auto dma_tile = [&](char *stage, int page, int jt) {
+        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
+        const int64_t pg = page >= 0 ? page : 0;
+        const int krec = page >= 0 ? (T::kRowBytes << log2P) : 0;
+        const int vrec = page >= 0 ? ((D * 2) << log2P) : 0;
+        const __amdgpu_buffer_rsrc_t rk = page_rsrc(kpool + ((pg * D) << log2P), krec);
+        const __amdgpu_buffer_rsrc_t rv = page_rsrc(vpool + ((pg * D) << log2P), vrec);
+#pragma unroll
+        for (int i = 0; i < T::kInstr; ++i)
+            dma16(rk, stage + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+#pragma unroll
+        for (int i = 0; i < T::vInstr; ++i)
+            dma16(rv, stage + T::kBytes + (wave * T::vInstr + i) * 1024, vdma[i], slot0 * 2);
+    };
+    // A tile that holds keys outside [zero_lo, zero_hi) gets those V^T entries
+    // zeroed once it has landed (their scores are masked, but 0 * NaN would
+    // still reach the accumulator).
+    auto edge_tile = [&](int jt) {
+        const int key0 = jt * kBK;
+        return key0 < zero_lo || key0 + kBK > zero_hi;
+    };
+    auto fixup = [&](char *stage, int jt) {
+        const int key0 = jt * kBK;
+        for (int e = threadIdx.x; e < D * kBK; e += kThreads) {
+            const int d = e / kBK, k = e % kBK, idx = key0 + k;
+            if (idx < zero_lo || idx >= zero_hi)
+                *reinterpret_cast<u16 *>(stage + T::kBytes + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
+        }
+    };
+
+    // Per-lane LDS operand addresses.
+    const int krow = swizzle_row(col);
+    unsigned ka[kSteps], va[4];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+        ka[s] = static_cast<unsigned>(krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) va[t] = static_cast<unsigned>(T::kBytes + col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
+
+    auto tile_active = [&](int jt) {
+        const int kp0 = k_pos0 + jt * kBK;
+        return wave_valid && kp0 <= wp_hi && !(window && kp0 + kBK - 1 < wp_lo - window + 1);
+    };
+    auto tile_full = [&](int jt) {
+        const int kp0 = k_pos0 + jt * kBK;
+        return (kp0 + kBK - 1 <= wp_lo) && (window == 0 || kp0 >= wp_hi - window + 1);
+    };
+
+    auto compute = [&](const char *stage, int jt) {
+        // S^T = K . Q^T: two 32-key accumulator chains, operands read 4 ahead.
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + ka[s] + kb * 32 * T::kRowBytes);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * kSteps - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+        if (!tile_full(jt)) {
+            const int kbase = k_pos0 + jt * kBK + 8 * half;
+            const unsigned span = static_cast<unsigned>(my_pos - lo_i);
+            const int off = kbase - lo_i;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jj = e >> 2, ii = e & 3;
+                    const int kc = 32 * kb + 16 * (jj >> 1) + 4 * (jj & 1) + ii;
+                    sacc[kb][e] = static_cast<unsigned>(off + kc) <= span ? sacc[kb][e] : -__builtin_inff();
+                }
+        }
+        float mt = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) mt = fmaxf(mt, fmaxf(sacc[0][e], sacc[0][e + 1]));
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mt = fmaxf(mt, fmaxf(sacc[1][e], sacc[1][e + 1]));
+        mt = max_halves(mt) * scale_log2;
+        if (__any(mt > m + kRescaleSlack)) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
+            m = m_new;
+        }
+
+        // P and O^T += V^T . P^T, 16 keys at a time: chunk t's probabilities feed
+        // the kDBlocks independent accumulators while chunk t+1's are computed.
+        float part[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 pb;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][8 * (t & 1) + i], scale_log2, -m));
+                acc += p;
+                pb[i] = static_cast<__bf16>(p);
+            }
+            part[t] = acc;
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + va[t] + db * 32 * 128);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+            }
+        }
+        lsum += (part[0] + part[1]) + (part[2] + part[3]);
+    };
+
+    auto iteration = [&](int jt, char *cur, char *nxt) {
+        const bool more = jt + 1 < tile_end;
+        int page_n = 0;
+        bool edge_n = false;
+        if (more) {
+            page_n = tile_page(jt + 1);
+            edge_n = edge_tile(jt + 1);
+            dma_tile(nxt, page_n, jt + 1);
+        }
+        if (tile_active(jt)) compute(cur, jt);
+        __syncthreads();
+        if (edge_n) {
+            fixup(nxt, jt + 1);
+            __syncthreads();
+        }
+    };
+
+    {
+        const int page0 = tile_page(tile_beg);
+        dma_tile(stage0, page0, tile_beg);
+        __syncthreads();
+        if (edge_tile(tile_beg)) {
+            fixup(stage0, tile_beg);
+            __syncthreads();
+        }
+    }
+    int jt = tile_beg;
+    for (; jt + 1 < tile_end; jt += 2) {
+        iteration(jt, stage0, stage1);
+        iteration(jt + 1, stage1, stage0);
+    }
+    if (jt < tile_end) iteration(jt, stage0, stage1);
+
+    const float ltot = sum_halves(lsum);
+    if (!row_ok) return;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    const int64_t obase = (my_row * hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int d0 = 32 * db + 8 * jj + 4 * half;
+            const float v0 = oacc[db][4 * jj + 0] * inv, v1 = oacc[db][4 * jj + 1] * inv;
+            const float v2 = oacc[db][4 * jj + 2] * inv, v3 = oacc[db][4 * jj + 3] * inv;
+            if constexpr (OUT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                bf16x4 w = {static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
+                            static_cast<__bf16>(v3)};
+                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) = w;
+            } else {
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
+            }
+        }
+    if (lse && half == 0)
+        lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
+}
+
 int log2_of(int p)
 {
     int l = 0;
@@ -485,7 +796,7 @@ template <int D, int HPW, bool OUT_BF16>
 void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
             hipStream_t stream)
 {
-    auto kernel = cfg.page_size >= kBK ? attn_prefill_kernel<D, HPW, OUT_BF16, true>
+    auto kernel = cfg.page_size >= kBK ? attn_prefill_dma_kernel<D, HPW, OUT_BF16>
                                        : attn_prefill_kernel<D, HPW, OUT_BF16, false>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(t.num_units)),
                        dim3(kThreads), 0, stream, static_cast<const u16 *>(q), static_cast<const u16 *>(cfg.k_pool),
