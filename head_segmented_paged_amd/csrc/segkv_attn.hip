@@ -29,10 +29,15 @@
 // operand is one 16-byte LDS read.
 //
 // Masking is index arithmetic on the tiles that cross the causal diagonal or
-// the window edge; tiles outside a wavefront's band are skipped, tiles inside
-// it run unmasked. Keys outside the segment's stored-and-visible range are
-// zero-filled in LDS so an undefined slot can never reach P.V.
+// the window edge; tiles inside a wavefront's band run unmasked. (The
+// register-staged kernel for small pages skips tiles outside the band; the
+// pipelined one computes them fully masked, which happens only at the band
+// edges of units with several row blocks.) Keys outside the segment's
+// stored-and-visible range are zero-filled in LDS so an undefined slot can
+// never reach P.V.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "segkv_internal.h"
 
@@ -99,6 +104,19 @@ __device__ __forceinline__ float sum_halves(float x)
 }
 
 // Physical page holding logical page lp of the segment, or -1.
+// acc + the sum of the eight bf16 values in x, as four bf16 dot products with
+// (1, 1): the softmax denominator then sums exactly the rounded probabilities
+// that multiply V, in half the instructions of eight fp32 adds.
+__device__ __forceinline__ float sum8_bf16(bf16x8 x, float acc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+}
+
 __device__ __forceinline__ int page_id(const int32_t *__restrict__ pages, int n_pages, int64_t num_pages, int lp)
 {
     const int id = pages[min(max(lp, 0), n_pages - 1)];
@@ -423,16 +441,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
                 for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
                 m = m_new;
             }
-            // P = exp2(S * scale * log2(e) - m), summed per lane, packed to bf16 B operands.
+            // P = exp2(S * scale * log2(e) - m), packed to bf16 B operands and summed per lane.
             bf16x8 pb[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], scale_log2, -m));
-                    lsum += p;
                     pb[2 * kb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
                 }
+            lsum += sum8_bf16(pb[0], 0.f) + sum8_bf16(pb[1], 0.f) + sum8_bf16(pb[2], 0.f) + sum8_bf16(pb[3], 0.f);
             // O^T += V^T . P^T, four 16-key steps.
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
@@ -514,8 +532,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const u16 *base, int
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16 *>(base), 0, bytes, 0x00020000);
 }
 
+// Software-pipelined kernel for pages of at least one tile (K and V tiles
+// DMA'd straight from the page into LDS, XOR-swizzled). K runs one tile
+// ahead of V: while a wavefront turns tile j's scores into probabilities and
+// accumulates P(j) V(j), it already issues the MFMAs for tile j+1's scores, so
+// the matrix cores have independent work during the softmax arithmetic.
+// Buffers: K(j+1) and V(j) are read while K(j+2) and V(j+1) land, two K and two
+// V tiles (the same 64 KB as two whole stages for D = 128).
 template <int D, int HPW, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
     int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
@@ -526,8 +551,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
     constexpr int kUnitRows = kWaveRows * kRowBlocks;
     constexpr int kSteps = D / 16;      // MFMA k-steps over the head dim for S^T
     constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(1024))) char stage0[T::bytes];
-    __shared__ __attribute__((aligned(1024))) char stage1[T::bytes];
+    // Separate arrays, so the compiler sees that a DMA into one buffer does not
+    // alias the LDS reads of another and adds no wait for it.
+    __shared__ __attribute__((aligned(1024))) char kbuf0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[T::vBytes];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[T::vBytes];
 
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS);
     const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
@@ -580,6 +609,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
     float m = kNegBig, lsum = 0.f;
 
     // Page ids: a 64-entry register window per wave, read with v_readlane.
+    // Lookups must come in non-decreasing tile order, at most one window apart.
     int win = ((tile_beg * kBK) >> log2P) >> 6;
     auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
     int win_cur = load_window(win), win_next = load_window(win + 1);
@@ -610,19 +640,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
     }
     // One buffer resource per page: an out-of-range offset, or a missing page
     // (zero records), reads as zeros.
-    auto dma_tile = [&](char *stage, int page, int jt) {
+    auto dma_k = [&](char *dst, int page, int jt) {
         const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
         const int64_t pg = page >= 0 ? page : 0;
-        const int krec = page >= 0 ? (T::kRowBytes << log2P) : 0;
-        const int vrec = page >= 0 ? ((D * 2) << log2P) : 0;
-        const __amdgpu_buffer_rsrc_t rk = page_rsrc(kpool + ((pg * D) << log2P), krec);
-        const __amdgpu_buffer_rsrc_t rv = page_rsrc(vpool + ((pg * D) << log2P), vrec);
+        const __amdgpu_buffer_rsrc_t rk =
+            page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
 #pragma unroll
         for (int i = 0; i < T::kInstr; ++i)
-            dma16(rk, stage + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+            dma16(rk, dst + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+    };
+    auto dma_v = [&](char *dst, int page, int jt) {
+        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
+        const int64_t pg = page >= 0 ? page : 0;
+        const __amdgpu_buffer_rsrc_t rv = page_rsrc(vpool + ((pg * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
 #pragma unroll
         for (int i = 0; i < T::vInstr; ++i)
-            dma16(rv, stage + T::kBytes + (wave * T::vInstr + i) * 1024, vdma[i], slot0 * 2);
+            dma16(rv, dst + (wave * T::vInstr + i) * 1024, vdma[i], slot0 * 2);
     };
     // A tile that holds keys outside [zero_lo, zero_hi) gets those V^T entries
     // zeroed once it has landed (their scores are masked, but 0 * NaN would
@@ -631,69 +664,73 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
         const int key0 = jt * kBK;
         return key0 < zero_lo || key0 + kBK > zero_hi;
     };
-    auto fixup = [&](char *stage, int jt) {
+    auto fixup = [&](char *vb, int jt) {
         const int key0 = jt * kBK;
         for (int e = threadIdx.x; e < D * kBK; e += kThreads) {
             const int d = e / kBK, k = e % kBK, idx = key0 + k;
             if (idx < zero_lo || idx >= zero_hi)
-                *reinterpret_cast<u16 *>(stage + T::kBytes + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
+                *reinterpret_cast<u16 *>(vb + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
         }
     };
 
-    // Per-lane LDS operand addresses.
+    // Per-lane LDS operand addresses within a K tile and a V^T tile.
     const int krow = swizzle_row(col);
     unsigned ka[kSteps], va[4];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
         ka[s] = static_cast<unsigned>(krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) va[t] = static_cast<unsigned>(T::kBytes + col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
+    for (int t = 0; t < 4; ++t) va[t] = static_cast<unsigned>(col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
 
-    auto tile_active = [&](int jt) {
-        const int kp0 = k_pos0 + jt * kBK;
-        return wave_valid && kp0 <= wp_hi && !(window && kp0 + kBK - 1 < wp_lo - window + 1);
-    };
     auto tile_full = [&](int jt) {
         const int kp0 = k_pos0 + jt * kBK;
         return (kp0 + kBK - 1 <= wp_lo) && (window == 0 || kp0 >= wp_hi - window + 1);
     };
 
-    auto compute = [&](const char *stage, int jt) {
-        // S^T = K . Q^T: two 32-key accumulator chains, operands read 4 ahead.
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // S^T k-step s of the next tile: two 32-key MFMAs.
+    auto score_step = [&](f32x16 (&sn)[2], const char *kb, int s) {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + ka[s] + kb * 32 * T::kRowBytes);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
-            }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * kSteps - 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int h = 0; h < 2; ++h) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + ka[s] + h * 32 * T::kRowBytes);
+            sn[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : sn[h], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // First k-steps of the next tile's scores go out before the masking and
+    // rescale branches; the rest are spread over the four probability chunks.
+    constexpr int kEarly = 2;
+    auto step_lo = [](int t) { return kEarly + (t * (kSteps - kEarly)) / 4; };
 
+    // One tile: scores sc of tile jt (already computed) -> P -> O^T += V^T P^T;
+    // when NEXT, the scores of tile jt + 1 from kn into sn on the side.
+    auto tile = [&](auto next, int jt, const char *kn, const char *vc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        constexpr bool NEXT = decltype(next)::value;
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int s = 0; s < kEarly; ++s) score_step(sn, kn, s);
+        }
         if (!tile_full(jt)) {
             const int kbase = k_pos0 + jt * kBK + 8 * half;
             const unsigned span = static_cast<unsigned>(my_pos - lo_i);
             const int off = kbase - lo_i;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int jj = e >> 2, ii = e & 3;
-                    const int kc = 32 * kb + 16 * (jj >> 1) + 4 * (jj & 1) + ii;
-                    sacc[kb][e] = static_cast<unsigned>(off + kc) <= span ? sacc[kb][e] : -__builtin_inff();
+                    const int kc = 32 * h + 16 * (jj >> 1) + 4 * (jj & 1) + ii;
+                    sc[h][e] = static_cast<unsigned>(off + kc) <= span ? sc[h][e] : -__builtin_inff();
                 }
         }
-        float mt = fmaxf(sacc[0][0], sacc[0][1]);
+        // Tile max: four independent chains of three-operand maxima.
+        float mx[4];
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) mt = fmaxf(mt, fmaxf(sacc[0][e], sacc[0][e + 1]));
+        for (int c = 0; c < 4; ++c) {
+            const int e0 = 8 * (c & 1);
+            mx[c] = fmaxf(sc[c >> 1][e0], sc[c >> 1][e0 + 1]);
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) mt = fmaxf(mt, fmaxf(sacc[1][e], sacc[1][e + 1]));
+            for (int e = 2; e < 8; e += 2) mx[c] = fmaxf(fmaxf(mx[c], sc[c >> 1][e0 + e]), sc[c >> 1][e0 + e + 1]);
+        }
+        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = max_halves(mt) * scale_log2;
         if (__any(mt > m + kRescaleSlack)) {
             const float m_new = fmaxf(m, mt);
@@ -703,62 +740,93 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_dma_kernel(
             for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
             m = m_new;
         }
-
-        // P and O^T += V^T . P^T, 16 keys at a time: chunk t's probabilities feed
-        // the kDBlocks independent accumulators while chunk t+1's are computed.
-        float part[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             bf16x8 pb;
-            float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][8 * (t & 1) + i], scale_log2, -m));
-                acc += p;
-                pb[i] = static_cast<__bf16>(p);
-            }
-            part[t] = acc;
+            for (int i = 0; i < 8; ++i)
+                pb[i] = static_cast<__bf16>(
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t >> 1][8 * (t & 1) + i], scale_log2, -m)));
+            lsum = sum8_bf16(pb, lsum);
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + va[t] + db * 32 * 128);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vc + va[t] + db * 32 * 128);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
             }
+            if constexpr (NEXT) {
+#pragma unroll
+                for (int s = step_lo(t); s < step_lo(t + 1); ++s) score_step(sn, kn, s);
+            }
         }
-        lsum += (part[0] + part[1]) + (part[2] + part[3]);
+        if constexpr (NEXT) {
+            // Operands read four MFMAs ahead; about four VALU ops beside each MFMA.
+            constexpr int kMfma = 4 * kDBlocks + 2 * (kSteps - kEarly);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < kMfma - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
     };
 
-    auto iteration = [&](int jt, char *cur, char *nxt) {
-        const bool more = jt + 1 < tile_end;
-        int page_n = 0;
-        bool edge_n = false;
-        if (more) {
-            page_n = tile_page(jt + 1);
-            edge_n = edge_tile(jt + 1);
-            dma_tile(nxt, page_n, jt + 1);
+    // Iteration jt: DMA V(jt+1) into vd and K(jt+2) into kd, compute tile jt
+    // (and the scores of jt+1 when it exists), then wait for the DMA.
+    int page_v = -1;   // page of tile jt+1, looked up when its K was fetched
+    auto iteration = [&](auto next, int jt, char *kn, char *vc, char *kd, char *vd, f32x16 (&sc)[2],
+                         f32x16 (&sn)[2]) {
+        constexpr bool NEXT = decltype(next)::value;
+        if constexpr (NEXT) {
+            dma_v(vd, page_v, jt + 1);
+            if (jt + 2 < tile_end) {
+                page_v = tile_page(jt + 2);
+                dma_k(kd, page_v, jt + 2);
+            }
         }
-        if (tile_active(jt)) compute(cur, jt);
-        __syncthreads();
-        if (edge_n) {
-            fixup(nxt, jt + 1);
+        tile(next, jt, kn, vc, sc, sn);
+        if constexpr (NEXT) {
             __syncthreads();
+            if (edge_tile(jt + 1)) {
+                fixup(vd, jt + 1);
+                __syncthreads();
+            }
         }
     };
 
+    f32x16 sa[2], sb[2];
     {
         const int page0 = tile_page(tile_beg);
-        dma_tile(stage0, page0, tile_beg);
-        __syncthreads();
-        if (edge_tile(tile_beg)) {
-            fixup(stage0, tile_beg);
-            __syncthreads();
+        dma_k(kbuf0, page0, tile_beg);
+        dma_v(vbuf0, page0, tile_beg);
+        if (tile_beg + 1 < tile_end) {
+            page_v = tile_page(tile_beg + 1);
+            dma_k(kbuf1, page_v, tile_beg + 1);
         }
+        __syncthreads();
+        if (edge_tile(tile_beg)) fixup(vbuf0, tile_beg);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) score_step(sa, kbuf0, s);
+        __syncthreads();   // kbuf0 is refilled by the first iteration
     }
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
     int jt = tile_beg;
-    for (; jt + 1 < tile_end; jt += 2) {
-        iteration(jt, stage0, stage1);
-        iteration(jt + 1, stage1, stage0);
+    for (; jt + 2 < tile_end; jt += 2) {
+        iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+        iteration(yes{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
     }
-    if (jt < tile_end) iteration(jt, stage0, stage1);
+    if (jt + 1 < tile_end) {
+        iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+        iteration(no{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
+    } else {
+        iteration(no{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+    }
 
     const float ltot = sum_halves(lsum);
     if (!row_ok) return;
@@ -796,7 +864,7 @@ template <int D, int HPW, bool OUT_BF16>
 void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
             hipStream_t stream)
 {
-    auto kernel = cfg.page_size >= kBK ? attn_prefill_dma_kernel<D, HPW, OUT_BF16>
+    auto kernel = cfg.page_size >= kBK ? attn_prefill_pipe_kernel<D, HPW, OUT_BF16>
                                        : attn_prefill_kernel<D, HPW, OUT_BF16, false>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(t.num_units)),
                        dim3(kThreads), 0, stream, static_cast<const u16 *>(q), static_cast<const u16 *>(cfg.k_pool),
