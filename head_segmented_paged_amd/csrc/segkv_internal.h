@@ -19,6 +19,11 @@ constexpr int kKvTile = 64;
 constexpr int kWaveRows = 32;
 // Wavefronts per attention workgroup.
 constexpr int kWaves = 4;
+// Work-list cohorts: XCDs of the device (workgroups are dealt to them
+// round-robin by index) and the workgroups one XCD holds at a time (32 CUs,
+// two attention workgroups each).
+constexpr int kXcds = 8;
+constexpr int kCohort = 64;
 
 // Shape of one attention work unit for a given GQA group size G: the
 // workgroup's four wavefronts cover `heads` query heads of one group times

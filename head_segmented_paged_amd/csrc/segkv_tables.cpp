@@ -7,7 +7,7 @@
 // one layer's class table, sequence lengths and block table (the
 // logical-to-physical page map of the KV-cache management page, section 3.1)
 // into the flat arrays the attention kernel reads, plus the kernel's work
-// list ordered longest-first.
+// list ordered longest-first in L2-sharing cohorts.
 #include <algorithm>
 #include <cstring>
 #include <limits>
@@ -174,12 +174,40 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         }
     }
     std::stable_sort(list.begin(), list.end(), [](const Unit &a, const Unit &b) { return a.tiles > b.tiles; });
-    for (size_t u = 0; u < list.size(); ++u) {
+
+    // Cohorts for the L2 caches. Workgroups go to the XCDs round-robin by
+    // index, and each XCD has its own L2. Consecutive windows of the sorted
+    // list (units of similar cost) are re-dealt so that every XCD receives
+    // neighbouring units in (segment, row) order: they start together and
+    // walk the same K/V tiles at about the same time, so one L2 fill serves
+    // them all instead of each unit refetching its window from HBM.
+    const size_t n_units = list.size();
+    const size_t window = static_cast<size_t>(segkv::kXcds) * segkv::kCohort;
+    std::vector<Unit> dealt(n_units);
+    for (size_t base = 0; base < n_units; base += window) {
+        const size_t n = std::min(window, n_units - base);
+        std::sort(list.begin() + base, list.begin() + base + n, [](const Unit &a, const Unit &b) {
+            if (a.seg != b.seg) return a.seg < b.seg;
+            if (a.row0 != b.row0) return a.row0 < b.row0;
+            return a.head0 < b.head0;
+        });
+        // Positions base + 8j + x belong to XCD x. The XCDs take the sorted
+        // window in turn, in reverse turn order every other window, so that
+        // no XCD always receives the costlier end of the windows (each XCD
+        // drains only its own share of the list).
+        const bool reverse = (base / window) % 2 == 1;
+        size_t idx = 0;
+        for (int t = 0; t < segkv::kXcds; ++t) {
+            const int x = reverse ? segkv::kXcds - 1 - t : t;
+            for (size_t p = x; p < n; p += segkv::kXcds) dealt[base + p] = list[base + idx++];
+        }
+    }
+    for (size_t u = 0; u < n_units; ++u) {
         int32_t *w = out->work + u * SEGKV_UNIT_FIELDS;
-        w[SEGKV_UNIT_SEGMENT] = list[u].seg;
-        w[SEGKV_UNIT_ROW0] = list[u].row0;
-        w[SEGKV_UNIT_HEAD0] = list[u].head0;
-        w[SEGKV_UNIT_TILES] = list[u].tiles;
+        w[SEGKV_UNIT_SEGMENT] = dealt[u].seg;
+        w[SEGKV_UNIT_ROW0] = dealt[u].row0;
+        w[SEGKV_UNIT_HEAD0] = dealt[u].head0;
+        w[SEGKV_UNIT_TILES] = dealt[u].tiles;
     }
     return SEGKV_OK;
 }

@@ -151,7 +151,10 @@ int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new
  * list: every (segment, row block, head block) once, ordered by descending
  * cost (KV tiles visited) so that a launch dispatches the longest units
  * first (longest-processing-time-first balance across heads of very unequal
- * length).
+ * length). The order is by cost between consecutive windows of 512 units
+ * only: inside a window the units are dealt so that positions x, x+8, x+16,
+ * ... (the workgroups one XCD receives) hold neighbours in (segment, row)
+ * order, which then share that XCD's L2.
  */
 typedef struct segkv_table_inputs {
     int32_t num_seqs;

@@ -40,13 +40,38 @@ def _compare(w, r, layer, ctx):
     return lib
 
 
+WINDOW = 512   # 8 XCDs x 64 workgroups: the cohort window of the work list
+
+
+def _check_order(work):
+    """Longest first between windows; inside a window, each XCD's share
+    (positions x, x+8, ...) in (segment, row, head) order."""
+    tiles = work[:, 3]
+    for a in range(0, len(work), WINDOW):
+        win = work[a:a + WINDOW]
+        if a + WINDOW < len(work):
+            assert tiles[a:a + WINDOW].min() >= tiles[a + WINDOW:].max()
+        for x in range(8):
+            share = win[x::8]
+            key = share[:, 0].astype(np.int64) * (1 << 40) + share[:, 1].astype(np.int64) * (1 << 12) + share[:, 2]
+            assert (np.diff(key) > 0).all()
+        # the XCDs' shares follow one another in (segment, row, head) order,
+        # XCD 0 first in even windows and XCD 7 first in odd ones
+        order = range(min(8, len(win)))
+        if (a // WINDOW) % 2 == 1:
+            order = [x for x in reversed(range(8)) if x < len(win)]
+        firsts = [tuple(win[x::8][0][:3]) for x in order]
+        lasts = [tuple(win[x::8][-1][:3]) for x in order]
+        for i in range(len(firsts) - 1):
+            assert lasts[i] < firsts[i + 1]
+
+
 def _check_work(lib, w):
     G = w.hq // w.hkv
     work = lib["work"]
     rows, heads = lib["unit_rows"], lib["unit_heads"]
     assert rows * heads == 128
-    # longest first
-    assert (np.diff(work[:, 3]) <= 0).all()
+    _check_order(work)
     # every (segment, head, row) exactly once
     for s in range(lib["num_segments"]):
         n = lib["n_q"][s]
@@ -82,7 +107,7 @@ def test_stack_all_layers():
         lib = _compare(w, r, layer, ctx)
         if layer in (0, 8, 63):
             work = lib["work"]
-            assert (np.diff(work[:, 3]) <= 0).all()
+            _check_order(work)
             assert len(work) == 8 * (131072 // 32)
 
 
