@@ -53,14 +53,18 @@ class LayerTables:
         self.H, self.torch, self.ctx = H, torch, ctx
         self.args = (r.cached_len, r.new_len, r.head_class[layer], r.window[layer], r.page_of[layer])
         host = H.segkv_build_head_tables(ctx, *self.args)
-        self.keys = ("seg_desc", "page_list", "work")
-        self.pin = {k: torch.empty(host[k].shape, dtype=torch.int32, pin_memory=True) for k in self.keys}
-        self.dev = {k: torch.empty(host[k].shape, dtype=torch.int32, device=device) for k in self.keys}
+        self.keys = ("seg_desc", "page_list", "work", "merge")
+        shape = {k: host[k].shape if host[k].size else (1, host[k].shape[-1]) for k in self.keys}
+        self.pin = {k: torch.empty(shape[k], dtype=torch.int32, pin_memory=True) for k in self.keys}
+        self.dev = {k: torch.empty(shape[k], dtype=torch.int32, device=device) for k in self.keys}
         self.pairs = host["total_pairs"]
+        # split-KV partial results (none on the 128K stack and the 32K layer)
+        self.workspace = torch.empty(max(host["workspace_bytes"], 1), dtype=torch.uint8, device=device)
         self.struct = S.segkv_dev_tables(
             self.dev["seg_desc"].data_ptr(), self.dev["page_list"].data_ptr(), self.dev["work"].data_ptr(),
             host["num_segments"], host["num_units"], host["num_page_entries"], host["total_q_rows"],
-            host["unit_rows"], host["unit_heads"])
+            host["unit_rows"], host["unit_heads"], self.dev["merge"].data_ptr(), host["num_merges"],
+            host["num_parts"])
         self.free = torch.cuda.Event()
         self.free.record()
 
@@ -68,7 +72,8 @@ class LayerTables:
         self.free.synchronize()            # the previous upload from the pinned buffers is done
         host = self.H.segkv_build_head_tables(self.ctx, *self.args)
         for k in self.keys:
-            self.pin[k].numpy()[...] = host[k]
+            if host[k].size:
+                self.pin[k].numpy()[...] = host[k]
             self.dev[k].copy_(self.pin[k], non_blocking=True)
         self.free.record()
         self.pairs = host["total_pairs"]
@@ -122,7 +127,7 @@ class Resident:
                                 max_new)
             if events is not None:
                 events[layer][1].record()
-            H.segkv_attn_prefill(self.ctx, lt, x["q"], self.o)
+            H.segkv_attn_prefill(self.ctx, lt, x["q"], self.o, workspace=lt.workspace)
             if events is not None:
                 events[layer][2].record()
 

@@ -85,7 +85,8 @@ extern "C" int segkv_gather_pages(const segkv_ctx *ctx, const int32_t *page_ids,
 }
 
 extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
-                                  int32_t o_dtype, float *lse, float softmax_scale, void *stream)
+                                  int32_t o_dtype, float *lse, float softmax_scale, void *workspace,
+                                  int64_t workspace_bytes, void *stream)
 {
     segkv::clear_error();
     if (!ctx || !t) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null argument");
@@ -96,12 +97,22 @@ extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *
     if (t->unit_rows != shape.rows || t->unit_heads != shape.heads)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: tables built for units of %d rows x %d heads, kernel "
                     "uses %d x %d", t->unit_rows, t->unit_heads, shape.rows, shape.heads);
-    if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0)
+    if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0 ||
+        t->num_merges < 0 || t->num_parts < 0)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: negative table size");
     if (t->num_units == 0) return SEGKV_OK;
     if (!t->seg_desc || !t->page_list || !t->work || !q || !o)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null pointer");
+    if (t->num_parts > 0 || t->num_merges > 0) {
+        if (cfg.page_size < 64)
+            return fail(SEGKV_ERR_UNSUPPORTED, "attn_prefill: split units need page_size >= 64");
+        if (t->num_merges > 0 && !t->merge) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null merge list");
+        const int64_t need = static_cast<int64_t>(t->num_parts) * SEGKV_PART_BYTES(cfg.head_dim);
+        if (!workspace || workspace_bytes < need)
+            return fail(SEGKV_ERR_CAPACITY, "attn_prefill: workspace of %lld bytes needed, %lld given",
+                        static_cast<long long>(need), static_cast<long long>(workspace ? workspace_bytes : 0));
+    }
     float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
     const float scale_log2 = scale * 1.44269504088896340736f;  // scores enter exp2 pre-multiplied by log2(e)
-    return segkv::launch_attn_prefill(cfg, *t, q, o, o_dtype, lse, scale_log2, stream);
+    return segkv::launch_attn_prefill(cfg, *t, q, o, o_dtype, lse, scale_log2, workspace, stream);
 }

@@ -544,7 +544,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
     int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
-    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse)
+    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse, float *__restrict__ parts,
+    int32_t num_parts)
 {
     using T = DmaTile<D>;
     constexpr int kRowBlocks = kWaves / HPW;
@@ -558,9 +559,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     __shared__ __attribute__((aligned(1024))) char vbuf0[T::vBytes];
     __shared__ __attribute__((aligned(1024))) char vbuf1[T::vBytes];
 
-    const i32x4 unit = *reinterpret_cast<const i32x4 *>(work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS);
+    const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
+    const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
     const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
-    if (seg < 0 || seg >= num_segments) return;
+    const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
+    const int part = unit2[SEGKV_UNIT_PART - 4];
+    if (seg < 0 || seg >= num_segments || part >= num_parts) return;
     const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
     const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
     const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
@@ -578,8 +583,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     const int unit_end = min(row0 + kUnitRows, n_q);
     const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
     const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
-    const int tile_beg = (lo_pos - k_pos0) / kBK;
-    const int tile_end = (last_pos + 1 - k_pos0 + kBK - 1) / kBK;
+    // The unit's run of tiles, within the band its rows see.
+    const int tile_beg = max((lo_pos - k_pos0) / kBK, run0);
+    const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
     const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
     const int zero_hi = k_len;
 
@@ -800,7 +806,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     };
 
     f32x16 sa[2], sb[2];
-    {
+    if (tile_beg < tile_end) {
         const int page0 = tile_page(tile_beg);
         dma_k(kbuf0, page0, tile_beg);
         dma_v(vbuf0, page0, tile_beg);
@@ -816,19 +822,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     }
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
-    int jt = tile_beg;
-    for (; jt + 2 < tile_end; jt += 2) {
-        iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
-        iteration(yes{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
-    }
-    if (jt + 1 < tile_end) {
-        iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
-        iteration(no{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
-    } else {
-        iteration(no{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+    if (tile_beg < tile_end) {
+        int jt = tile_beg;
+        for (; jt + 2 < tile_end; jt += 2) {
+            iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+            iteration(yes{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
+        }
+        if (jt + 1 < tile_end) {
+            iteration(yes{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+            iteration(no{}, jt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sb, sa);
+        } else {
+            iteration(no{}, jt, kbuf1, vbuf0, kbuf0, vbuf1, sa, sb);
+        }
     }
 
     const float ltot = sum_halves(lsum);
+    if (part >= 0) {
+        // Split unit: unnormalised O, running maximum and sum to its slot:
+        // [128 (wave, row)][D] outputs, then [128] maxima, then [128] sums.
+        float *slot = parts + static_cast<int64_t>(part) * (kWaves * kWaveRows * (D + 2));
+        const int r = wave * kWaveRows + col;
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<f32x4 *>(slot + r * D + 32 * db + 8 * jj + 4 * half) =
+                    f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+        if (half == 0) {
+            slot[kWaves * kWaveRows * D + r] = m;
+            slot[kWaves * kWaveRows * (D + 1) + r] = ltot;
+        }
+        return;
+    }
     if (!row_ok) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     const int64_t obase = (my_row * hq + head) * D;
@@ -853,6 +879,64 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
         lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
+// Merge pass for split blocks (split-KV): one workgroup per merge entry, one
+// (query row, head) per pair of lanes, each lane half of the head dim. The
+// runs' partial results combine exactly as blocks of one online softmax:
+// O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void merge_parts_kernel(
+    const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
+    const float *__restrict__ parts, int32_t num_parts, int32_t heads_per_unit, int32_t total_q_rows, int32_t hq,
+    void *__restrict__ o, float *__restrict__ lse)
+{
+    const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
+    const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
+    const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
+    if (seg < 0 || seg >= num_segments || part0 < 0 || nparts < 1 || part0 > num_parts - nparts) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+    const int head = head0 + wave % heads_per_unit;
+    const int t = row0 + (wave / heads_per_unit) * kWaveRows + col;
+    if (t >= n_q || head >= hq) return;
+    const int64_t row = static_cast<int64_t>(q_row0) + t;
+    if (row >= total_q_rows) return;
+    constexpr int kSlot = kWaves * kWaveRows * (D + 2);   // floats per partial result
+    constexpr int kHalf = D / 2;
+    const int r = wave * kWaveRows + col;
+    const float *base = parts + static_cast<int64_t>(part0) * kSlot;
+    float mmax = kNegBig;
+    for (int p = 0; p < nparts; ++p) mmax = fmaxf(mmax, base[p * kSlot + kWaves * kWaveRows * D + r]);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 acc[kHalf / 4];
+#pragma unroll
+    for (int i = 0; i < kHalf / 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+        const float *slot = base + p * kSlot;
+        const float w = __builtin_amdgcn_exp2f(slot[kWaves * kWaveRows * D + r] - mmax);
+        l += w * slot[kWaves * kWaveRows * (D + 1) + r];
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + r * D + half * kHalf);
+#pragma unroll
+        for (int i = 0; i < kHalf / 4; ++i) acc[i] += w * src[i];
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t obase = (row * hq + head) * D + half * kHalf;
+#pragma unroll
+    for (int i = 0; i < kHalf / 4; ++i) {
+        const f32x4 v = acc[i] * inv;
+        if constexpr (OUT_BF16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + 4 * i) =
+                bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                       static_cast<__bf16>(v[3])};
+        } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + 4 * i) = v;
+        }
+    }
+    if (lse && half == 0) lse[static_cast<int64_t>(head) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+}
+
 int log2_of(int p)
 {
     int l = 0;
@@ -862,48 +946,58 @@ int log2_of(int p)
 
 template <int D, int HPW, bool OUT_BF16>
 void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
-            hipStream_t stream)
+            float *parts, hipStream_t stream)
 {
-    auto kernel = cfg.page_size >= kBK ? attn_prefill_pipe_kernel<D, HPW, OUT_BF16>
-                                       : attn_prefill_kernel<D, HPW, OUT_BF16, false>;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(t.num_units)),
-                       dim3(kThreads), 0, stream, static_cast<const u16 *>(q), static_cast<const u16 *>(cfg.k_pool),
-                       static_cast<const u16 *>(cfg.v_pool), cfg.num_pages, log2_of(cfg.page_size), t.seg_desc,
-                       t.page_list, t.num_page_entries, t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads,
-                       scale_log2, o, lse);
+    const dim3 grid(static_cast<unsigned>(t.num_units)), block(kThreads);
+    const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
+    const u16 *vp = static_cast<const u16 *>(cfg.v_pool);
+    const int log2P = log2_of(cfg.page_size);
+    if (cfg.page_size >= kBK)
+        hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16>), grid, block, 0, stream, qh, kp, vp,
+                           cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
+                           t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts, t.num_parts);
+    else
+        hipLaunchKernelGGL((attn_prefill_kernel<D, HPW, OUT_BF16, false>), grid, block, 0, stream, qh, kp, vp,
+                           cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
+                           t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse);
+    if (t.num_merges > 0)
+        hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges)), block, 0,
+                           stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_heads,
+                           t.total_q_rows, cfg.num_q_heads, o, lse);
 }
 
 template <int D, int HPW>
 void launch_dtype(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                  float *lse, float scale_log2, hipStream_t stream)
+                  float *lse, float scale_log2, float *parts, hipStream_t stream)
 {
     if (o_dtype == SEGKV_DTYPE_BF16)
-        launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, stream);
+        launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, parts, stream);
     else
-        launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, stream);
+        launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, parts, stream);
 }
 
 template <int D>
 void launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                  float *lse, float scale_log2, hipStream_t stream)
+                  float *lse, float scale_log2, float *parts, hipStream_t stream)
 {
     switch (t.unit_heads) {
-    case 4: launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
-    case 2: launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
-    default: launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, stream); break;
+    case 4: launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
+    case 2: launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
+    default: launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
     }
 }
 
 }  // namespace
 
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
-                        int32_t o_dtype, float *lse, float scale_log2, void *stream)
+                        int32_t o_dtype, float *lse, float scale_log2, void *workspace, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    float *parts = static_cast<float *>(workspace);
     if (cfg.head_dim == 128)
-        launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, s);
+        launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
     else
-        launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, s);
+        launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: %s", hipGetErrorString(err));
     return SEGKV_OK;

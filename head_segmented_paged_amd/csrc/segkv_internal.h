@@ -24,6 +24,8 @@ constexpr int kWaves = 4;
 // two attention workgroups each).
 constexpr int kXcds = 8;
 constexpr int kCohort = 64;
+// Shortest run the automatic split-KV policy cuts a block into (tiles).
+constexpr int kMinRun = 16;
 
 // Shape of one attention work unit for a given GQA group size G: the
 // workgroup's four wavefronts cover `heads` query heads of one group times
@@ -49,6 +51,6 @@ int launch_write_pages(const segkv_config &cfg, const void *k_new, const void *v
 int launch_gather_pages(const segkv_config &cfg, const int32_t *page_ids, int64_t n, void *k_out, void *v_out,
                         void *stream);
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
-                        int32_t o_dtype, float *lse, float scale_log2, void *stream);
+                        int32_t o_dtype, float *lse, float scale_log2, void *workspace, void *stream);
 
 }  // namespace segkv

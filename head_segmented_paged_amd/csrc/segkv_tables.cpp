@@ -23,6 +23,11 @@ struct Seg {
     int64_t pairs;
 };
 
+// One work unit: a block (segment, row block, head block) over a run of its tiles.
+struct Unit {
+    int32_t seg, row0, head0, tiles, tile0, part;
+};
+
 // Sum over the n new rows i = c .. c+n-1 of the number of visible keys,
 // min(i + 1, W) for a local head (W > 0) or i + 1 for a global head (W == 0).
 int64_t visible_pairs(int64_t c, int64_t n, int64_t W)
@@ -108,6 +113,70 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     if (units > std::numeric_limits<int32_t>::max())
         return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: too many work units");
 
+    // Blocks: every (segment, row block, head block) once, with the run of
+    // 64-key tiles its rows see (tile0 counted from the segment's k_pos0).
+    std::vector<Unit> list;
+    list.reserve(static_cast<size_t>(units));
+    int64_t total_tiles = 0, longest = 0;
+    for (int32_t s = 0; s < static_cast<int32_t>(segs.size()); ++s) {
+        const Seg &sg = segs[s];
+        for (int32_t r0 = 0; r0 < sg.n_q; r0 += shape.rows) {
+            const int64_t first = static_cast<int64_t>(sg.q_pos0) + r0;
+            const int64_t last = static_cast<int64_t>(sg.q_pos0) + std::min(r0 + shape.rows, sg.n_q) - 1;
+            const int64_t lo = sg.window == 0 ? 0 : std::max<int64_t>(0, first - sg.window + 1);
+            const int64_t kbeg = lo - sg.k_pos0, kend = last + 1 - sg.k_pos0;
+            const int32_t tile0 = static_cast<int32_t>(kbeg / segkv::kKvTile);
+            const int32_t tiles = static_cast<int32_t>((kend + segkv::kKvTile - 1) / segkv::kKvTile) - tile0;
+            for (int32_t h = 0; h < G; h += shape.heads) {
+                list.push_back(Unit{s, r0, sg.kv_head * G + h, tiles, tile0, -1});
+                total_tiles += tiles;
+                longest = std::max<int64_t>(longest, tiles);
+            }
+        }
+    }
+
+    // Split-KV: cut long blocks into runs when list scheduling alone could not
+    // balance them (a block longer than the mean load of a workgroup slot
+    // finishes after everything else however the list is ordered).
+    int64_t max_run = 0;   // 0: no split
+    if (P >= segkv::kKvTile && in->max_unit_tiles >= 0) {
+        if (in->max_unit_tiles > 0) {
+            max_run = in->max_unit_tiles;
+        } else {
+            const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::kCohort;
+            if (4 * longest * slots > 3 * total_tiles)
+                max_run = std::max<int64_t>(segkv::kMinRun, (total_tiles + 2 * slots - 1) / (2 * slots));
+        }
+    }
+    std::vector<int32_t> merges;   // [num_merges][SEGKV_MERGE_FIELDS]
+    int64_t n_parts = 0;
+    if (max_run > 0 && longest > max_run) {
+        std::vector<Unit> cut;
+        cut.reserve(list.size());
+        for (const Unit &u : list) {
+            if (u.tiles <= max_run) {
+                cut.push_back(u);
+                continue;
+            }
+            const int64_t nr = (u.tiles + max_run - 1) / max_run;
+            const int32_t merge[SEGKV_MERGE_FIELDS] = {u.seg, u.row0, u.head0, static_cast<int32_t>(n_parts),
+                                                       static_cast<int32_t>(nr), 0, 0, 0};
+            merges.insert(merges.end(), merge, merge + SEGKV_MERGE_FIELDS);
+            for (int64_t r = 0; r < nr; ++r) {   // runs of near-equal length
+                const int64_t a = u.tiles * r / nr, b = u.tiles * (r + 1) / nr;
+                cut.push_back(Unit{u.seg, u.row0, u.head0, static_cast<int32_t>(b - a),
+                                   static_cast<int32_t>(u.tile0 + a), static_cast<int32_t>(n_parts + r)});
+            }
+            n_parts += nr;
+        }
+        list.swap(cut);
+        if (static_cast<int64_t>(list.size()) > std::numeric_limits<int32_t>::max() ||
+            n_parts > std::numeric_limits<int32_t>::max())
+            return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: too many split units");
+    }
+    units = static_cast<int64_t>(list.size());
+    const int32_t n_merges = static_cast<int32_t>(merges.size() / SEGKV_MERGE_FIELDS);
+
     const int32_t nseg = static_cast<int32_t>(segs.size());
     out->num_segments = nseg;
     out->num_units = static_cast<int32_t>(units);
@@ -116,12 +185,16 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     out->total_q_rows = static_cast<int32_t>(q_rows);
     out->unit_rows = shape.rows;
     out->unit_heads = shape.heads;
-    if (out->seg_cap < nseg || out->seq_cap < S || out->page_cap < pages || out->unit_cap < units)
+    out->num_merges = n_merges;
+    out->num_parts = static_cast<int32_t>(n_parts);
+    out->workspace_bytes = n_parts * SEGKV_PART_BYTES(cfg.head_dim);
+    if (out->seg_cap < nseg || out->seq_cap < S || out->page_cap < pages || out->unit_cap < units ||
+        out->merge_cap < n_merges)
         return fail(SEGKV_ERR_CAPACITY, "build_head_tables: buffers too small (need %d segments, %d sequences, "
-                    "%lld page entries, %lld units)", nseg, S, static_cast<long long>(pages),
-                    static_cast<long long>(units));
+                    "%lld page entries, %lld units, %d merges)", nseg, S, static_cast<long long>(pages),
+                    static_cast<long long>(units), n_merges);
     if (!out->seg_desc || !out->cu_seqlens_q || !out->cu_seqlens_k || !out->cu_pages || !out->page_list ||
-        !out->pairs || !out->work)
+        !out->pairs || !out->work || (n_merges > 0 && !out->merge))
         return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: null output buffer");
 
     // Segment arrays, prefix sums and the page list.
@@ -153,26 +226,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     out->cu_seqlens_q[0] = 0;
     for (int32_t b = 0; b < S; ++b) out->cu_seqlens_q[b + 1] = out->cu_seqlens_q[b] + in->new_len[b];
 
-    // Work list: every (segment, row block, head block) once, with its cost in
-    // KV tiles; then longest first, ties in generation order.
-    struct Unit {
-        int32_t seg, row0, head0, tiles;
-    };
-    std::vector<Unit> list;
-    list.reserve(static_cast<size_t>(units));
-    for (int32_t s = 0; s < nseg; ++s) {
-        const Seg &sg = segs[s];
-        for (int32_t r0 = 0; r0 < sg.n_q; r0 += shape.rows) {
-            const int64_t first = static_cast<int64_t>(sg.q_pos0) + r0;
-            const int64_t last = static_cast<int64_t>(sg.q_pos0) + std::min(r0 + shape.rows, sg.n_q) - 1;
-            const int64_t lo = sg.window == 0 ? 0 : std::max<int64_t>(0, first - sg.window + 1);
-            const int64_t kbeg = lo - sg.k_pos0, kend = last + 1 - sg.k_pos0;
-            const int32_t tiles = static_cast<int32_t>((kend + segkv::kKvTile - 1) / segkv::kKvTile -
-                                                       kbeg / segkv::kKvTile);
-            for (int32_t h = 0; h < G; h += shape.heads)
-                list.push_back(Unit{s, r0, sg.kv_head * G + h, tiles});
-        }
-    }
+    // Work list: longest first, then dealt to the XCDs in cohorts.
     std::stable_sort(list.begin(), list.end(), [](const Unit &a, const Unit &b) { return a.tiles > b.tiles; });
 
     // Cohorts for the L2 caches. Workgroups go to the XCDs round-robin by
@@ -189,7 +243,8 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         std::sort(list.begin() + base, list.begin() + base + n, [](const Unit &a, const Unit &b) {
             if (a.seg != b.seg) return a.seg < b.seg;
             if (a.row0 != b.row0) return a.row0 < b.row0;
-            return a.head0 < b.head0;
+            if (a.head0 != b.head0) return a.head0 < b.head0;
+            return a.tile0 < b.tile0;
         });
         // Positions base + 8j + x belong to XCD x. The XCDs take the sorted
         // window in turn, in reverse turn order every other window, so that
@@ -208,6 +263,11 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         w[SEGKV_UNIT_ROW0] = dealt[u].row0;
         w[SEGKV_UNIT_HEAD0] = dealt[u].head0;
         w[SEGKV_UNIT_TILES] = dealt[u].tiles;
+        w[SEGKV_UNIT_TILE0] = dealt[u].tile0;
+        w[SEGKV_UNIT_PART] = dealt[u].part;
+        w[6] = 0;
+        w[7] = 0;
     }
+    if (n_merges > 0) std::memcpy(out->merge, merges.data(), sizeof(int32_t) * merges.size());
     return SEGKV_OK;
 }

@@ -23,7 +23,13 @@ SEGKV_ERR_UNSUPPORTED = -5
 SEGKV_DTYPE_F32 = 0
 SEGKV_DTYPE_BF16 = 1
 SEG_FIELDS = 8
-UNIT_FIELDS = 4
+UNIT_FIELDS = 8
+MERGE_FIELDS = 8
+
+
+def part_bytes(head_dim):
+    """Workspace bytes per split-KV partial result (SEGKV_PART_BYTES)."""
+    return 512 * (head_dim + 2)
 SEG_FIELD_NAMES = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len", "page_off")
 
 _P = ctypes.c_void_p
@@ -38,7 +44,7 @@ class segkv_config(ctypes.Structure):
 
 class segkv_table_inputs(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("max_lp", _i32), ("cached_len", _P), ("new_len", _P),
-                ("head_class", _P), ("window", _P), ("page_of", _P)]
+                ("head_class", _P), ("window", _P), ("page_of", _P), ("max_unit_tiles", _i32)]
 
 
 class segkv_tables(ctypes.Structure):
@@ -46,12 +52,15 @@ class segkv_tables(ctypes.Structure):
                 ("num_segments", _i32), ("num_units", _i32), ("num_page_entries", _i64), ("total_pairs", _i64),
                 ("total_q_rows", _i32), ("unit_rows", _i32), ("unit_heads", _i32),
                 ("seg_desc", _P), ("cu_seqlens_q", _P), ("cu_seqlens_k", _P), ("cu_pages", _P),
-                ("page_list", _P), ("pairs", _P), ("work", _P)]
+                ("page_list", _P), ("pairs", _P), ("work", _P),
+                ("merge_cap", _i32), ("num_merges", _i32), ("num_parts", _i32), ("workspace_bytes", _i64),
+                ("merge", _P)]
 
 
 class segkv_dev_tables(ctypes.Structure):
     _fields_ = [("seg_desc", _P), ("page_list", _P), ("work", _P), ("num_segments", _i32), ("num_units", _i32),
-                ("num_page_entries", _i64), ("total_q_rows", _i32), ("unit_rows", _i32), ("unit_heads", _i32)]
+                ("num_page_entries", _i64), ("total_q_rows", _i32), ("unit_rows", _i32), ("unit_heads", _i32),
+                ("merge", _P), ("num_merges", _i32), ("num_parts", _i32)]
 
 
 class SegKVError(RuntimeError):
@@ -70,8 +79,8 @@ def _load():
         "segkv_write_pages": ([_P, _P, _P, _i64, _P, _P, _P, _i32, _i32, _i32, _P], ctypes.c_int),
         "segkv_build_head_tables": ([_P, ctypes.POINTER(segkv_table_inputs), ctypes.POINTER(segkv_tables)],
                                     ctypes.c_int),
-        "segkv_attn_prefill": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P],
-                               ctypes.c_int),
+        "segkv_attn_prefill": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P, _i64,
+                                _P], ctypes.c_int),
         "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
         "segkv_last_error": ([], ctypes.c_char_p),
         "segkv_version": ([], ctypes.c_char_p),
@@ -164,14 +173,16 @@ def segkv_write_pages(ctx, k_new, v_new, cu_rows, pos0, page_of, max_rows_per_se
                                   _stream(stream)))
 
 
-def segkv_build_head_tables(ctx, cached_len, new_len, head_class, window, page_of):
-    """Host arrays in, dict of host numpy arrays out (see segkv_tables in the header)."""
+def segkv_build_head_tables(ctx, cached_len, new_len, head_class, window, page_of, max_unit_tiles=0):
+    """Host arrays in, dict of host numpy arrays out (see segkv_tables in the header).
+    max_unit_tiles: split-KV policy (0 automatic, > 0 longest run in tiles, < 0 never)."""
     c = np.ascontiguousarray(cached_len, dtype=np.int32)
     n = np.ascontiguousarray(new_len, dtype=np.int32)
     cls = np.ascontiguousarray(head_class, dtype=np.int8)
     win = np.ascontiguousarray(window, dtype=np.int32)
     po = np.ascontiguousarray(page_of, dtype=np.int32)
-    inp = segkv_table_inputs(c.shape[0], po.shape[-1], _ptr(c), _ptr(n), _ptr(cls), _ptr(win), _ptr(po))
+    inp = segkv_table_inputs(c.shape[0], po.shape[-1], _ptr(c), _ptr(n), _ptr(cls), _ptr(win), _ptr(po),
+                             int(max_unit_tiles))
     out = segkv_tables()
     rc = _lib.segkv_build_head_tables(ctx.handle, ctypes.byref(inp), ctypes.byref(out))
     if rc not in (SEGKV_OK, SEGKV_ERR_CAPACITY):
@@ -185,18 +196,21 @@ def segkv_build_head_tables(ctx, cached_len, new_len, head_class, window, page_o
         "page_list": np.zeros(max(out.num_page_entries, 1), np.int32),
         "pairs": np.zeros(S, np.int64),
         "work": np.zeros((max(out.num_units, 1), UNIT_FIELDS), np.int32),
+        "merge": np.zeros((max(out.num_merges, 1), MERGE_FIELDS), np.int32),
     }
     out2 = segkv_tables(S, c.shape[0], bufs["page_list"].shape[0], bufs["work"].shape[0])
+    out2.merge_cap = bufs["merge"].shape[0]
     for k, v in bufs.items():
         setattr(out2, k, _ptr(v))
     _check(_lib.segkv_build_head_tables(ctx.handle, ctypes.byref(inp), ctypes.byref(out2)))
     res = dict(bufs)
     res["page_list"] = res["page_list"][:out2.num_page_entries]
     res["work"] = res["work"][:out2.num_units]
+    res["merge"] = res["merge"][:out2.num_merges]
     for i, name in enumerate(SEG_FIELD_NAMES):
         res[name] = res["seg_desc"][:, i].copy()
     for k in ("num_segments", "num_units", "num_page_entries", "total_pairs", "total_q_rows",
-              "unit_rows", "unit_heads"):
+              "unit_rows", "unit_heads", "num_merges", "num_parts", "workspace_bytes"):
         res[k] = int(getattr(out2, k))
     return res
 
@@ -211,18 +225,25 @@ class DevTables:
         self.page_list = torch.from_numpy(np.ascontiguousarray(pl)).to(device)
         wk = host["work"] if host["work"].size else np.zeros((1, UNIT_FIELDS), np.int32)
         self.work = torch.from_numpy(np.ascontiguousarray(wk)).to(device)
+        mg = host["merge"] if host["merge"].size else np.zeros((1, MERGE_FIELDS), np.int32)
+        self.merge = torch.from_numpy(np.ascontiguousarray(mg)).to(device)
+        self.workspace_bytes = host["workspace_bytes"]
         self.host = host
         self.struct = segkv_dev_tables(_ptr(self.seg_desc), _ptr(self.page_list), _ptr(self.work),
                                        host["num_segments"], host["num_units"], host["num_page_entries"],
-                                       host["total_q_rows"], host["unit_rows"], host["unit_heads"])
+                                       host["total_q_rows"], host["unit_rows"], host["unit_heads"],
+                                       _ptr(self.merge), host["num_merges"], host["num_parts"])
 
 
 def upload_tables(host, device="cuda"):
     return DevTables(host, device)
 
 
-def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None):
-    """q bf16 [rows][hq][D]; o fp32 or bf16 [rows][hq][D]; lse fp32 [hq][rows] or None."""
+def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None, workspace=None):
+    """q bf16 [rows][hq][D]; o fp32 or bf16 [rows][hq][D]; lse fp32 [hq][rows] or None.
+    workspace: device buffer of at least the tables' workspace_bytes (split-KV
+    partial results); when None and the tables need one, a torch buffer is
+    allocated for the call."""
     import torch
     if o.dtype == torch.float32:
         dt = SEGKV_DTYPE_F32
@@ -230,8 +251,12 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
         dt = SEGKV_DTYPE_BF16
     else:
         raise TypeError("o must be float32 or bfloat16")
+    need = int(dev_tables.struct.num_parts) * part_bytes(ctx.cfg.head_dim)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
-                                   _ptr(lse), float(softmax_scale), _stream(stream)))
+                                   _ptr(lse), float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def segkv_gather_pages(ctx, page_ids, k_out, v_out, stream=None):

@@ -80,14 +80,35 @@ enum {
 
 /* Fields of one work unit (int32 [num_units][SEGKV_UNIT_FIELDS]). A unit is
  * one workgroup of the attention kernel: unit_rows consecutive query rows of
- * one segment for unit_heads consecutive query heads of its GQA group. */
+ * one segment for unit_heads consecutive query heads of its GQA group, over
+ * a run of the 64-key tiles those rows see. A block whose run is split into
+ * several units (split-KV) writes partial results to the workspace, and one
+ * merge entry per block combines them. */
 enum {
     SEGKV_UNIT_SEGMENT = 0,
     SEGKV_UNIT_ROW0 = 1,    /* first query row, relative to the segment (0 .. n_b-1) */
     SEGKV_UNIT_HEAD0 = 2,   /* first query head (absolute) */
     SEGKV_UNIT_TILES = 3,   /* KV tiles the unit visits: its cost, used to order the list */
-    SEGKV_UNIT_FIELDS = 4
+    SEGKV_UNIT_TILE0 = 4,   /* first tile, counted in 64-key steps from the segment's k_pos0 */
+    SEGKV_UNIT_PART = 5,    /* workspace slot of a split unit's partial result, -1 = writes O */
+    SEGKV_UNIT_FIELDS = 8   /* fields 6, 7 are zero */
 };
+
+/* Fields of one merge entry (int32 [num_merges][SEGKV_MERGE_FIELDS]): the
+ * block of a split unit and its partial results, workspace slots
+ * part0 .. part0 + nparts - 1. */
+enum {
+    SEGKV_MERGE_SEGMENT = 0,
+    SEGKV_MERGE_ROW0 = 1,
+    SEGKV_MERGE_HEAD0 = 2,
+    SEGKV_MERGE_PART0 = 3,
+    SEGKV_MERGE_NPARTS = 4,
+    SEGKV_MERGE_FIELDS = 8  /* fields 5 .. 7 are zero */
+};
+
+/* Workspace bytes per partial result: 128 (query row, head) pairs, each with
+ * head_dim unnormalised fp32 outputs plus its running maximum and sum. */
+#define SEGKV_PART_BYTES(head_dim) (512 * ((int64_t)(head_dim) + 2))
 
 typedef struct segkv_ctx segkv_ctx;
 
@@ -155,6 +176,15 @@ int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new
  * only: inside a window the units are dealt so that positions x, x+8, x+16,
  * ... (the workgroups one XCD receives) hold neighbours in (segment, row)
  * order, which then share that XCD's L2.
+ *
+ * Split-KV (page_size >= 64 only). With max_unit_tiles == 0 the builder splits
+ * when the longest block would visit more than 3/4 of the mean tiles per
+ * workgroup slot (512 slots): then every block longer than
+ * max(16, ceil(mean / 2)) tiles is cut into equal runs of at most that many.
+ * max_unit_tiles > 0 cuts every block longer than that; < 0 never splits.
+ * A split block's runs become separate units with workspace slots, and one
+ * merge entry per block; segkv_attn_prefill then needs workspace_bytes =
+ * num_parts * SEGKV_PART_BYTES(head_dim) of device workspace.
  */
 typedef struct segkv_table_inputs {
     int32_t num_seqs;
@@ -164,6 +194,7 @@ typedef struct segkv_table_inputs {
     const int8_t *head_class;   /* [hkv] 1 = global, 0 = local (this layer) */
     const int32_t *window;      /* [hkv] W >= 1 for local heads; ignored for global */
     const int32_t *page_of;     /* [num_seqs][hkv][max_lp] (this layer) */
+    int32_t max_unit_tiles;     /* split-KV policy: 0 automatic, > 0 longest run, < 0 never */
 } segkv_table_inputs;
 
 typedef struct segkv_tables {
@@ -188,6 +219,12 @@ typedef struct segkv_tables {
     int32_t *page_list;         /* [page_cap] */
     int64_t *pairs;             /* [seg_cap] */
     int32_t *work;              /* [unit_cap][SEGKV_UNIT_FIELDS] */
+    /* split-KV (appended): capacity, sizes, buffer */
+    int32_t merge_cap;          /* merge entries (set by the caller) */
+    int32_t num_merges;
+    int32_t num_parts;          /* workspace slots */
+    int64_t workspace_bytes;    /* num_parts * SEGKV_PART_BYTES(head_dim) */
+    int32_t *merge;             /* [merge_cap][SEGKV_MERGE_FIELDS] */
 } segkv_tables;
 
 int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_inputs *in, segkv_tables *out);
@@ -203,6 +240,9 @@ typedef struct segkv_dev_tables {
     int32_t total_q_rows;
     int32_t unit_rows;          /* must equal the builder's values for this context */
     int32_t unit_heads;
+    const int32_t *merge;       /* device [num_merges][SEGKV_MERGE_FIELDS], or NULL if none */
+    int32_t num_merges;
+    int32_t num_parts;
 } segkv_dev_tables;
 
 /*
@@ -213,13 +253,21 @@ typedef struct segkv_dev_tables {
  *   lse : device fp32 [hq][total_q_rows] natural-log sum of exp of the scaled
  *         scores, or NULL
  *   softmax_scale : multiplies q.k; <= 0 selects 1/sqrt(head_dim)
+ *   workspace : device memory of at least t->num_parts * SEGKV_PART_BYTES(head_dim)
+ *               bytes (caller-owned; may be NULL when num_parts == 0). Its
+ *               contents need no initialisation and are scratch afterwards;
+ *               calls that share a workspace must not overlap.
  * For query row t of segment s and query head h of its group, position
  * i = q_pos0 + t:  O = sum_j softmax_j(scale * q.k_j) v_j over the visible
  * keys j of i, computed with bf16 inputs, fp32 accumulation and an online
- * (running-maximum) softmax. Every output row is written exactly once.
+ * (running-maximum) softmax. Every output row is written exactly once: by its
+ * unit, or, for a split block, by the merge pass that combines the runs'
+ * partial results (O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r, M the
+ * largest running maximum), launched on the same stream right after.
  */
 int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
-                       int32_t o_dtype, float *lse, float softmax_scale, void *stream);
+                       int32_t o_dtype, float *lse, float softmax_scale, void *workspace,
+                       int64_t workspace_bytes, void *stream);
 
 /*
  * Read pages back in a dense layout (tests, debugging):

@@ -25,8 +25,10 @@ def device_pools(num_pages, P, D, fill=0.0, device="cuda"):
 class GpuLayer:
     """One layer of a realized workload on the GPU."""
 
-    def __init__(self, w, r, layer, tensors, page_of=None, poison=False, device="cuda", pools=None):
+    def __init__(self, w, r, layer, tensors, page_of=None, poison=False, device="cuda", pools=None,
+                 max_unit_tiles=0):
         self.w, self.r, self.layer = w, r, layer
+        self.max_unit_tiles = max_unit_tiles
         self.page_of = (r.page_of[layer] if page_of is None else page_of).astype(np.int32)
         if pools is None:
             pools = device_pools(r.num_pages, w.page, w.d, float("nan") if poison else 0.0, device)
@@ -50,7 +52,7 @@ class GpuLayer:
     def tables(self):
         r = self.r
         self.host = H.segkv_build_head_tables(self.ctx, r.cached_len, r.new_len, r.head_class[self.layer],
-                                              r.window[self.layer], self.page_of)
+                                              r.window[self.layer], self.page_of, self.max_unit_tiles)
         self.dev = H.upload_tables(self.host, self.device)
         return self.host
 

@@ -11,6 +11,7 @@ import pytest
 
 import head_segmented_paged_amd as H
 from head_segmented_paged_amd import segkv as S
+from tests.common import adhoc
 from workloads import TINY, realize
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "segkv.h")
@@ -116,15 +117,42 @@ def test_attn_prefill_validates_before_launch():
     host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0])
     dt = S.segkv_dev_tables(1, 2, 3, host["num_segments"], host["num_units"], host["num_page_entries"],
                             host["total_q_rows"], host["unit_rows"] * 2, host["unit_heads"])
-    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, None)
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, None, 0, None)
     assert rc == S.SEGKV_ERR_INVALID_ARG and "units" in H.segkv_last_error()
     dt.unit_rows = host["unit_rows"]
-    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, 7, None, 0.0, None)
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, 7, None, 0.0, None, 0, None)
     assert rc == S.SEGKV_ERR_INVALID_ARG
-    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), None, 5, S.SEGKV_DTYPE_F32, None, 0.0, None)
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), None, 5, S.SEGKV_DTYPE_F32, None, 0.0, None, 0, None)
     assert rc == S.SEGKV_ERR_INVALID_ARG
-    rc = S._lib.segkv_attn_prefill(None, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, None)
+    rc = S._lib.segkv_attn_prefill(None, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, None, 0, None)
     assert rc == S.SEGKV_ERR_INVALID_ARG
+
+
+def test_split_tables_need_a_workspace():
+    w = adhoc(hq=4, hkv=1, d=128, page=64, window=64, classes=(1,), seqs=((0, 300),), seed=5)
+    r = realize(w)
+    ctx = _ctx(w.hq, w.hkv, w.d, w.page, r.num_pages)
+    host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
+                                     max_unit_tiles=2)
+    assert host["num_parts"] > 0 and host["num_merges"] > 0
+    assert host["workspace_bytes"] == host["num_parts"] * 512 * (w.d + 2)
+    dt = S.segkv_dev_tables(1, 2, 3, host["num_segments"], host["num_units"], host["num_page_entries"],
+                            host["total_q_rows"], host["unit_rows"], host["unit_heads"], 9, host["num_merges"],
+                            host["num_parts"])
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, None, 0, None)
+    assert rc == S.SEGKV_ERR_CAPACITY and "workspace" in H.segkv_last_error()
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, 8,
+                                   host["workspace_bytes"] - 1, None)
+    assert rc == S.SEGKV_ERR_CAPACITY
+    dt.merge = None
+    rc = S._lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, 8,
+                                   host["workspace_bytes"], None)
+    assert rc == S.SEGKV_ERR_INVALID_ARG and "merge" in H.segkv_last_error()
+    # pages shorter than a tile: the builder never splits, hand-made split tables are refused
+    ctx16 = _ctx(4, 1, 128, 16, 64)
+    rc = S._lib.segkv_attn_prefill(ctx16.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, 8,
+                                   host["workspace_bytes"], None)
+    assert rc == S.SEGKV_ERR_UNSUPPORTED
 
 
 def test_write_and_gather_validate_before_launch():

@@ -106,8 +106,34 @@ def test_ragged_all_rows(case):
     run_case(adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * d + page))
 
 
+SPLIT = [
+    # (hq, hkv, d, page, window, classes, seqs, longest run in tiles)
+    (8, 2, 128, 64, 100, (0, 1), ((0, 200), (37, 301), (1000, 77)), 1),
+    (16, 2, 64, 128, 300, (0, 0), ((250, 260), (0, 1)), 2),
+    (6, 3, 128, 256, 40, (1, 0, 0), ((700, 45), (3, 250)), 3),
+    (4, 4, 64, 64, 1, (1, 1, 0, 0), ((0, 400), (130, 7)), 2),
+    (4, 1, 128, 64, 500, (1,), ((900, 160),), 5),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_run{c[7]}")
+def test_split_kv_all_rows(case):
+    """Blocks cut into short runs: partial results through the workspace and the
+    merge pass, every row against the oracle; bf16 output is RNE of fp32."""
+    hq, hkv, d, page, window, classes, seqs, run = case
+    w = adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * d + run)
+    o, lse, gl = run_case(w, max_unit_tiles=run)
+    assert gl.host["num_parts"] > 0 and gl.host["num_merges"] > 0
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+
+
 def test_mistral_8k_sampled():
-    run_case(MISTRAL_8K, queries="sampled", seed=2)
+    """The 8K layer is split automatically (its longest block exceeds the mean
+    load per workgroup slot)."""
+    o, lse, gl = run_case(MISTRAL_8K, queries="sampled", seed=2)
+    assert gl.host["num_parts"] > 0
 
 
 def test_llama70b_32k_sampled():

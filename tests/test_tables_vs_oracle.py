@@ -52,16 +52,15 @@ def _check_order(work):
         if a + WINDOW < len(work):
             assert tiles[a:a + WINDOW].min() >= tiles[a + WINDOW:].max()
         for x in range(8):
-            share = win[x::8]
-            key = share[:, 0].astype(np.int64) * (1 << 40) + share[:, 1].astype(np.int64) * (1 << 12) + share[:, 2]
-            assert (np.diff(key) > 0).all()
+            share = [tuple(int(v) for v in u[[0, 1, 2, 4]]) for u in win[x::8]]
+            assert all(a < b for a, b in zip(share, share[1:]))
         # the XCDs' shares follow one another in (segment, row, head) order,
         # XCD 0 first in even windows and XCD 7 first in odd ones
         order = range(min(8, len(win)))
         if (a // WINDOW) % 2 == 1:
             order = [x for x in reversed(range(8)) if x < len(win)]
-        firsts = [tuple(win[x::8][0][:3]) for x in order]
-        lasts = [tuple(win[x::8][-1][:3]) for x in order]
+        firsts = [tuple(win[x::8][0][[0, 1, 2, 4]]) for x in order]
+        lasts = [tuple(win[x::8][-1][[0, 1, 2, 4]]) for x in order]
         for i in range(len(firsts) - 1):
             assert lasts[i] < firsts[i + 1]
 
@@ -71,24 +70,44 @@ def _check_work(lib, w):
     work = lib["work"]
     rows, heads = lib["unit_rows"], lib["unit_heads"]
     assert rows * heads == 128
+    assert (work[:, 6:] == 0).all()
     _check_order(work)
-    # every (segment, head, row) exactly once
+    # blocks: every (segment, head, row) in exactly one block; a block's units
+    # cut its natural run of tiles into consecutive pieces
+    blocks = {}
+    for u in work:
+        blocks.setdefault((int(u[0]), int(u[1]), int(u[2])), []).append(u)
     for s in range(lib["num_segments"]):
         n = lib["n_q"][s]
         g = lib["kv_head"][s]
         cnt = np.zeros((G, n), np.int32)
-        mine = work[work[:, 0] == s]
-        for seg, r0, h0, _ in mine:
+        for (seg, r0, h0) in [b for b in blocks if b[0] == s]:
             assert g * G <= h0 and h0 + heads <= (g + 1) * G and r0 % rows == 0
             cnt[h0 - g * G: h0 - g * G + heads, r0: min(r0 + rows, n)] += 1
         assert (cnt == 1).all()
-    # the cost is the number of 64-key tiles between the first visible key of
-    # the unit's first row and the last row's own key
-    for seg, r0, h0, tiles in work[:: max(1, len(work) // 500)]:
+    merges = {(int(m[0]), int(m[1]), int(m[2])): m for m in lib["merge"]}
+    assert len(merges) == lib["num_merges"] == len(lib["merge"])
+    assert (lib["merge"][:, 5:] == 0).all() if len(lib["merge"]) else True
+    seen_parts = []
+    for key, units in blocks.items():
+        seg, r0, h0 = key
         c, W, k0 = lib["q_pos0"][seg], lib["window"][seg], lib["k_pos0"][seg]
         last = c + min(r0 + rows, lib["n_q"][seg]) - 1
         lo = 0 if W == 0 else max(0, c + r0 - W + 1)
-        assert tiles == -(-(last + 1 - k0) // 64) - (lo - k0) // 64
+        t0, t1 = (lo - k0) // 64, -(-(last + 1 - k0) // 64)
+        runs = sorted((int(u[4]), int(u[3]), int(u[5])) for u in units)
+        assert runs[0][0] == t0 and runs[-1][0] + runs[-1][1] == t1
+        for (a, na, _), (b, _, _) in zip(runs, runs[1:]):
+            assert a + na == b and na >= 1
+        if len(runs) == 1:
+            assert runs[0][2] == -1 and key not in merges
+        else:
+            m = merges[key]
+            parts = sorted(r[2] for r in runs)
+            assert parts == list(range(m[3], m[3] + m[4]))
+            seen_parts += parts
+    assert sorted(seen_parts) == list(range(lib["num_parts"]))
+    assert lib["workspace_bytes"] == lib["num_parts"] * 512 * (w.d + 2)
 
 
 @pytest.mark.parametrize("w", [x for x in ALL if x.layers == 1], ids=lambda w: w.name)
@@ -113,6 +132,47 @@ def test_stack_all_layers():
 
 SMALL = [((0, 1),), ((0, 17),), ((5, 30),), ((37, 100),), ((0, 100), (37, 15), (5, 2)),
          ((16, 16), (15, 1)), ((100, 20),), ((64, 64),), ((3, 13), (0, 50), (200, 33))]
+
+
+@pytest.mark.parametrize("max_run", [1, 2, 3, 7])
+@pytest.mark.parametrize("seqs", [((0, 300),), ((100, 20),), ((0, 100), (37, 15), (5, 2)), ((200, 130), (3, 13))])
+@pytest.mark.parametrize("page", [16, 64])
+def test_forced_splits(max_run, seqs, page):
+    w = adhoc(hq=8, hkv=2, d=64, page=page, window=70, classes=(1, 0), seqs=seqs, seed=max_run + page)
+    r = realize(w)
+    ctx = _ctx(w, r.num_pages)
+    lib = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
+                                    max_unit_tiles=max_run)
+    lib.update({k: lib["seg_desc"][:, i] for i, k in enumerate(("q_row0", "n_q", "q_pos0", "kv_head", "window",
+                                                                "k_pos0", "k_len", "page_off"))})
+    _check_work(lib, w)
+    if page < 64:
+        assert lib["num_parts"] == 0          # the small-page kernel has no split path
+    else:
+        never = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0],
+                                          r.page_of[0], max_unit_tiles=-1)
+        assert (lib["work"][:, 3] <= max_run).all()
+        assert (lib["num_parts"] > 0) == (never["work"][:, 3].max() > max_run)
+
+
+def test_automatic_split_policy():
+    """Splits exactly where list scheduling cannot balance: the 8K layer's longest
+    block (128 tiles) exceeds 3/4 of the mean load per workgroup slot."""
+    by = {x.name: x for x in ALL}
+    for name, expect in (("mistral7b_like_l8192", True), ("llama70b_like_l32768", False),
+                         ("varlen16_chunk2048", False), ("tiny_gqa2_l512", False)):
+        w = by[name]
+        r = realize(w)
+        ctx = _ctx(w, r.num_pages)
+        lib = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0],
+                                        r.page_of[0])
+        assert (lib["num_parts"] > 0) == expect, name
+        if expect:
+            total = int(lib["work"][:, 3].sum())
+            assert lib["work"][:, 3].max() <= max(16, -(-total // 1024)) + 1
+        never = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0],
+                                          r.page_of[0], max_unit_tiles=-1)
+        assert never["num_parts"] == 0
 
 
 @pytest.mark.parametrize("seqs", SMALL)
