@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # Sources whose change invalidates the committed HBM counter figures: the
 # attention kernel and the work-list order that decides its cache reuse.
 TRAFFIC_SOURCES = ("head_segmented_paged_amd/csrc/segkv_attn.hip", "head_segmented_paged_amd/csrc/segkv_tables.cpp")
@@ -293,6 +294,17 @@ def main():
     attn_step = attn.sum(axis=1)                      # ms per step, attention launches only
     write_step = write.sum(axis=1)
     achieved = res.flops_per_step / (float(np.mean(attn_step)) / 1e3) / 1e12
+    algo_bytes = algorithmic_bytes(w, res.r, 2 if args.o_dtype == "bf16" else 4)
+    # A decode step (a few new rows per sequence) moves far more bytes than it
+    # computes: its roofline is HBM bandwidth, not the matrix cores.
+    decode = int(res.r.new_len.max()) <= 8
+    if decode:
+        roof = {"bound": "hbm", "achieved": algo_bytes * w.layers / (float(np.mean(attn_step)) / 1e3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name)
     value = res.flops_per_step / wall / 1e12
     r = res.r
     globals_per_layer = r.head_class.sum(axis=1).tolist()
@@ -322,15 +334,8 @@ def main():
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "visible_pairs_per_step": res.pairs_per_step,
         "useful_flops_per_step": res.flops_per_step,
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(w.name),
-        },
-        "algorithmic_bytes_per_launch": algorithmic_bytes(w, r, 2 if args.o_dtype == "bf16" else 4),
+        "roofline": roof,
+        "algorithmic_bytes_per_launch": algo_bytes,
         "globals_per_layer": globals_per_layer,
     }
     if not args.no_secondary and w.name == "stack64_l131072":

@@ -93,10 +93,14 @@ extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *
     const segkv_config &cfg = ctx->cfg;
     if (o_dtype != SEGKV_DTYPE_F32 && o_dtype != SEGKV_DTYPE_BF16)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: o_dtype must be SEGKV_DTYPE_F32 or SEGKV_DTYPE_BF16");
-    const segkv::UnitShape shape = segkv::unit_shape(cfg.num_q_heads / cfg.num_kv_heads);
-    if (t->unit_rows != shape.rows || t->unit_heads != shape.heads)
-        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: tables built for units of %d rows x %d heads, kernel "
-                    "uses %d x %d", t->unit_rows, t->unit_heads, shape.rows, shape.heads);
+    const int G = cfg.num_q_heads / cfg.num_kv_heads;
+    const segkv::UnitShape shape = segkv::unit_shape(G, cfg.page_size);
+    const bool decode_ok = segkv::decode_units(G, cfg.page_size, 1) && t->unit_rows == segkv::decode_shape(G).rows &&
+                           t->unit_heads == segkv::decode_shape(G).heads;
+    if ((t->unit_rows != shape.rows || t->unit_heads != shape.heads) && !decode_ok)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: tables built for units of %d rows x %d heads, kernels "
+                    "use %d x %d (or %d x %d for decode with pages >= 64)", t->unit_rows, t->unit_heads, shape.rows,
+                    shape.heads, segkv::decode_shape(G).rows, segkv::decode_shape(G).heads);
     if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0 ||
         t->num_merges < 0 || t->num_parts < 0)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: negative table size");
@@ -107,7 +111,8 @@ extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *
         if (cfg.page_size < 64)
             return fail(SEGKV_ERR_UNSUPPORTED, "attn_prefill: split units need page_size >= 64");
         if (t->num_merges > 0 && !t->merge) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null merge list");
-        const int64_t need = static_cast<int64_t>(t->num_parts) * SEGKV_PART_BYTES(cfg.head_dim);
+        const int64_t need =
+            static_cast<int64_t>(t->num_parts) * SEGKV_PART_BYTES(t->unit_rows, t->unit_heads, cfg.head_dim);
         if (!workspace || workspace_bytes < need)
             return fail(SEGKV_ERR_CAPACITY, "attn_prefill: workspace of %lld bytes needed, %lld given",
                         static_cast<long long>(need), static_cast<long long>(workspace ? workspace_bytes : 0));

@@ -839,9 +839,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     const float ltot = sum_halves(lsum);
     if (part >= 0) {
         // Split unit: unnormalised O, running maximum and sum to its slot:
-        // [128 (wave, row)][D] outputs, then [128] maxima, then [128] sums.
-        float *slot = parts + static_cast<int64_t>(part) * (kWaves * kWaveRows * (D + 2));
-        const int r = wave * kWaveRows + col;
+        // [pairs][D] outputs, then [pairs] maxima, then [pairs] sums, pair
+        // r = (head offset) * unit rows + (row offset).
+        constexpr int kPairs = kUnitRows * HPW;   // (row, head) pairs per unit
+        float *slot = parts + static_cast<int64_t>(part) * (kPairs * (D + 2));
+        const int r = (wave % HPW) * kUnitRows + (wave / HPW) * kWaveRows + col;
         typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db)
@@ -850,8 +852,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
                 *reinterpret_cast<f32x4 *>(slot + r * D + 32 * db + 8 * jj + 4 * half) =
                     f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
         if (half == 0) {
-            slot[kWaves * kWaveRows * D + r] = m;
-            slot[kWaves * kWaveRows * (D + 1) + r] = ltot;
+            slot[kPairs * D + r] = m;
+            slot[kPairs * (D + 1) + r] = ltot;
         }
         return;
     }
@@ -879,51 +881,292 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
         lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
-// Merge pass for split blocks (split-KV): one workgroup per merge entry, one
-// (query row, head) per pair of lanes, each lane half of the head dim. The
-// runs' partial results combine exactly as blocks of one online softmax:
-// O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
+// Decode / small-chunk kernel (pages of at least one tile). A unit is one
+// segment's few new rows for all G query heads of its KV head: column c of
+// the MFMAs is the (row c / G, head c % G) pair, so the 32 columns carry up to
+// 32 / G rows. The unit's run of 64-key tiles is read two tiles (128 keys) at
+// a time into a two-stage LDS ring, and each wavefront takes its own 32 keys
+// of the pair: wave w reads keys 32 (w & 1) .. +31 of tile (w >> 1). Each wave
+// keeps its own running maximum, sum and O^T; at the end the four combine
+// through LDS as blocks of one online softmax. The step is bound by HBM
+// bandwidth, and the 128 KB ring keeps 64 KB of K/V in flight per CU.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void merge_parts_kernel(
-    const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
-    const float *__restrict__ parts, int32_t num_parts, int32_t heads_per_unit, int32_t total_q_rows, int32_t hq,
-    void *__restrict__ o, float *__restrict__ lse)
+__global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
+    int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
+    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
+    int32_t hq, int32_t unit_rows, int32_t unit_heads, float scale_log2, void *__restrict__ o,
+    float *__restrict__ lse, float *__restrict__ parts, int32_t num_parts)
 {
-    const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
-    const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
-    const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
-    if (seg < 0 || seg >= num_segments || part0 < 0 || nparts < 1 || part0 > num_parts - nparts) return;
+    using T = DmaTile<D>;
+    constexpr int kSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    constexpr int kLd = D + 4;   // floats per (wave, column) row of the combine buffer
+    __shared__ __attribute__((aligned(1024))) char stage0[2 * T::bytes];
+    __shared__ __attribute__((aligned(1024))) char stage1[2 * T::bytes];
+
+    const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
+    const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
+    const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
+    const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
+    const int part = unit2[SEGKV_UNIT_PART - 4];
+    if (seg < 0 || seg >= num_segments || part >= num_parts || unit_heads < 1 || unit_rows < 1 ||
+        unit_rows * unit_heads > kWaveRows)
+        return;
     const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
-    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
-    const int head = head0 + wave % heads_per_unit;
-    const int t = row0 + (wave / heads_per_unit) * kWaveRows + col;
-    if (t >= n_q || head >= hq) return;
-    const int64_t row = static_cast<int64_t>(q_row0) + t;
-    if (row >= total_q_rows) return;
-    constexpr int kSlot = kWaves * kWaveRows * (D + 2);   // floats per partial result
-    constexpr int kHalf = D / 2;
-    const int r = wave * kWaveRows + col;
-    const float *base = parts + static_cast<int64_t>(part0) * kSlot;
-    float mmax = kNegBig;
-    for (int p = 0; p < nparts; ++p) mmax = fmaxf(mmax, base[p * kSlot + kWaves * kWaveRows * D + r]);
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
+    int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
+    if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
+    const int32_t *pages = page_list + page_off;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const int sub = wave >> 1, kh = wave & 1;   // this wave's tile of the pair and 32-key half
+
+    // Rows of the unit and its band of tiles, cut to the unit's run.
+    const int unit_end = min(row0 + unit_rows, n_q);
+    const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
+    const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
+    const int tile_beg = max((lo_pos - k_pos0) / kBK, run0);
+    const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
+    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
+    const int zero_hi = k_len;
+
+    // This lane's column: (row, head) pair, its query position and the keys it
+    // may see inside the run.
+    const int pr = col / unit_heads, ph = col % unit_heads;
+    const bool col_ok = col < unit_rows * unit_heads && row0 + pr < n_q && head0 + ph < hq;
+    const int my_t = min(row0 + pr, n_q - 1);
+    const int head = min(head0 + ph, hq - 1);
+    const int my_pos = q_pos0 + my_t;
+    const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
+    const int run_lo = k_pos0 + tile_beg * kBK, run_hi = k_pos0 + tile_end * kBK - 1;
+    const int lo_eff = max(window ? my_pos - window + 1 : 0, run_lo);
+    const int hi_eff = min(my_pos, run_hi);
+    // Keys every column may see (tiles inside need no mask).
+    const int all_lo = max(window ? last_pos - window + 1 : 0, run_lo);
+    const int all_hi = min(first_pos, run_hi);
+
+    bf16x8 qreg[kSteps];
+    {
+        const bool can_load = col_ok && my_row < total_q_rows;
+        const u16 *qp = q + (my_row * hq + head) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+            qreg[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    f32x16 oacc[kDBlocks];
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
+    float m = kNegBig, lsum = 0.f;
+
+    int win = ((tile_beg * kBK) >> log2P) >> 6;
+    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
+    int win_cur = load_window(win), win_next = load_window(win + 1);
+    auto tile_page = [&](int jt) {
+        const int lp = (jt * kBK) >> log2P;
+        if ((lp >> 6) != win) {
+            win = lp >> 6;
+            win_cur = win_next;
+            win_next = load_window(win + 1);
+        }
+        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
+        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    };
+
+    unsigned kdma[T::kInstr], vdma[T::vInstr];
+#pragma unroll
+    for (int i = 0; i < T::kInstr; ++i) {
+        const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
+        const int r = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(r);
+        kdma[i] = static_cast<unsigned>(r * T::kRowBytes + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < T::vInstr; ++i) {
+        const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
+        const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
+        vdma[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
+    }
+    // Tiles jt and jt + 1 into one stage (a tile past the run reads zeros).
+    auto dma_pair = [&](char *stage, int jt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tj = jt + i;
+            const int page = tj < tile_end ? tile_page(tj) : -1;
+            const unsigned slot0 = static_cast<unsigned>((tj * kBK) & ((1 << log2P) - 1));
+            const int64_t pg = page >= 0 ? page : 0;
+            const __amdgpu_buffer_rsrc_t rk =
+                page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
+            const __amdgpu_buffer_rsrc_t rv =
+                page_rsrc(vpool + ((pg * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
+            char *dst = stage + i * T::bytes;
+#pragma unroll
+            for (int k = 0; k < T::kInstr; ++k)
+                dma16(rk, dst + (wave * T::kInstr + k) * 1024, kdma[k], slot0 * T::kRowBytes);
+#pragma unroll
+            for (int k = 0; k < T::vInstr; ++k)
+                dma16(rv, dst + T::kBytes + (wave * T::vInstr + k) * 1024, vdma[k], slot0 * 2);
+        }
+    };
+    auto edge_pair = [&](int jt) {
+        const int key0 = jt * kBK;
+        return key0 < zero_lo || key0 + 2 * kBK > zero_hi;
+    };
+    auto fixup_pair = [&](char *stage, int jt) {
+        for (int e = threadIdx.x; e < 2 * D * kBK; e += kThreads) {
+            const int i = e / (D * kBK), d = (e / kBK) % D, k = e % kBK, idx = (jt + i) * kBK + k;
+            if (idx < zero_lo || idx >= zero_hi)
+                *reinterpret_cast<u16 *>(stage + i * T::bytes + T::kBytes + d * 128 + (((k >> 3) ^ vswz(d)) << 4) +
+                                         (k & 7) * 2) = 0;
+        }
+    };
+
+    const int krow = kh * 32 + swizzle_row(col);
+    unsigned ka[kSteps], va[2];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+        ka[s] = static_cast<unsigned>(sub * T::bytes + krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        va[t] = static_cast<unsigned>(sub * T::bytes + T::kBytes + col * 128 +
+                                      (((2 * (2 * kh + t) + half) ^ vswz(col)) << 4));
+
+    auto compute = [&](const char *stage, int jt) {
+        f32x16 sacc = {};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + ka[s]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc, 0, 0, 0);
+        }
+        // Keys of this wave: k_pos0 + (jt + sub) * 64 + 32 kh + 16 t + 8 half + i.
+        const int kp0 = k_pos0 + (jt + sub) * kBK + kh * 32;
+        if (!(kp0 >= all_lo && kp0 + 31 <= all_hi)) {
+            const int kbase = kp0 + 8 * half;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int pos = kbase + 16 * (e >> 3) + (e & 7);
+                sacc[e] = (pos >= lo_eff && pos <= hi_eff) ? sacc[e] : -__builtin_inff();
+            }
+        }
+        float mx = fmaxf(sacc[0], sacc[1]);
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, sacc[e]), sacc[e + 1]);
+        const float mt = max_halves(mx) * scale_log2;
+        if (__any(mt > m + kRescaleSlack)) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
+            m = m_new;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 pb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * t + i], scale_log2, -m)));
+            lsum = sum8_bf16(pb, lsum);
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + va[t] + db * 32 * 128);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    if (tile_beg < tile_end) {
+        dma_pair(stage0, tile_beg);
+        __syncthreads();
+        if (edge_pair(tile_beg)) {
+            fixup_pair(stage0, tile_beg);
+            __syncthreads();
+        }
+        auto iteration = [&](int jt, char *cur, char *nxt) {
+            const bool more = jt + 2 < tile_end;
+            if (more) dma_pair(nxt, jt + 2);
+            compute(cur, jt);
+            __syncthreads();
+            if (more && edge_pair(jt + 2)) {
+                fixup_pair(nxt, jt + 2);
+                __syncthreads();
+            }
+        };
+        int jt = tile_beg;
+        for (; jt + 2 < tile_end; jt += 4) {
+            iteration(jt, stage0, stage1);
+            iteration(jt + 2, stage1, stage0);
+        }
+        if (jt < tile_end) iteration(jt, stage0, stage1);
+    }
+
+    // Combine the four waves' partial softmax states through LDS (the ring is
+    // free: the last barrier has passed). Wave w's row c: [D] outputs, m, l.
+    const float ltot = sum_halves(lsum);
+    float *cbuf = reinterpret_cast<float *>(wave < 2 ? stage0 : stage1) + (wave & 1) * kWaveRows * kLd;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 acc[kHalf / 4];
 #pragma unroll
-    for (int i = 0; i < kHalf / 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float *slot = base + p * kSlot;
-        const float w = __builtin_amdgcn_exp2f(slot[kWaves * kWaveRows * D + r] - mmax);
-        l += w * slot[kWaves * kWaveRows * (D + 1) + r];
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + r * D + half * kHalf);
+    for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int i = 0; i < kHalf / 4; ++i) acc[i] += w * src[i];
+        for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<f32x4 *>(cbuf + col * kLd + 32 * db + 8 * jj + 4 * half) =
+                f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+    if (half == 0) {
+        cbuf[col * kLd + D] = m;
+        cbuf[col * kLd + D + 1] = ltot;
+    }
+    __syncthreads();
+
+    // 8 threads per column, D / 8 outputs each.
+    constexpr int kPer = D / 8;
+    const int c = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * kPer;
+    const float *w0 = reinterpret_cast<const float *>(stage0), *w2 = reinterpret_cast<const float *>(stage1);
+    const float *src[4] = {w0 + c * kLd, w0 + (kWaveRows + c) * kLd, w2 + c * kLd, w2 + (kWaveRows + c) * kLd};
+    float mmax = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mmax = fmaxf(mmax, src[w][D]);
+    float wgt[4], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        wgt[w] = __builtin_amdgcn_exp2f(src[w][D] - mmax);
+        l += wgt[w] * src[w][D + 1];
+    }
+    f32x4 acc[kPer / 4];
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[i] += wgt[w] * *reinterpret_cast<const f32x4 *>(src[w] + d0 + 4 * i);
+    }
+    const int cr = c / unit_heads, ch = c % unit_heads;
+    if (c >= unit_rows * unit_heads || row0 + cr >= n_q || head0 + ch >= hq) return;
+    const int64_t row = static_cast<int64_t>(q_row0) + row0 + cr;
+    if (row >= total_q_rows) return;
+    const int hd = head0 + ch;
+    if (part >= 0) {
+        // Split unit: its combined unnormalised O, maximum and sum go to the
+        // workspace slot, pair r = (head offset) * unit_rows + (row offset).
+        const int pairs = unit_rows * unit_heads, r = ch * unit_rows + cr;
+        float *slot = parts + static_cast<int64_t>(part) * pairs * (D + 2);
+#pragma unroll
+        for (int i = 0; i < kPer / 4; ++i) *reinterpret_cast<f32x4 *>(slot + r * D + d0 + 4 * i) = acc[i];
+        if ((threadIdx.x & 7) == 0) {
+            slot[pairs * D + r] = mmax;
+            slot[pairs * (D + 1) + r] = l;
+        }
+        return;
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t obase = (row * hq + head) * D + half * kHalf;
+    const int64_t obase = (row * hq + hd) * D + d0;
 #pragma unroll
-    for (int i = 0; i < kHalf / 4; ++i) {
+    for (int i = 0; i < kPer / 4; ++i) {
         const f32x4 v = acc[i] * inv;
         if constexpr (OUT_BF16) {
             typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -934,7 +1177,68 @@ __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
             *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + 4 * i) = v;
         }
     }
-    if (lse && half == 0) lse[static_cast<int64_t>(head) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+    if (lse && (threadIdx.x & 7) == 0)
+        lse[static_cast<int64_t>(hd) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+}
+
+// Merge pass for split blocks (split-KV): one workgroup per merge entry, two
+// lanes per (query row, head) pair, each lane half of the head dim. The runs'
+// partial results combine exactly as blocks of one online softmax:
+// O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void merge_parts_kernel(
+    const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
+    const float *__restrict__ parts, int32_t num_parts, int32_t unit_rows, int32_t unit_heads,
+    int32_t total_q_rows, int32_t hq, void *__restrict__ o, float *__restrict__ lse)
+{
+    const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
+    const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
+    const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
+    if (seg < 0 || seg >= num_segments || part0 < 0 || nparts < 1 || part0 > num_parts - nparts) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q];
+    const int pairs = unit_rows * unit_heads;
+    const int64_t kSlot = static_cast<int64_t>(pairs) * (D + 2);   // floats per partial result
+    constexpr int kHalf = D / 2;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    for (int item = threadIdx.x; item < 2 * pairs; item += kThreads) {
+        const int r = item >> 1, half = item & 1;
+        const int head = head0 + r / unit_rows, t = row0 + r % unit_rows;
+        if (t >= n_q || head >= hq) continue;
+        const int64_t row = static_cast<int64_t>(q_row0) + t;
+        if (row >= total_q_rows) continue;
+        const float *base = parts + static_cast<int64_t>(part0) * kSlot;
+        float mmax = kNegBig;
+        for (int p = 0; p < nparts; ++p) mmax = fmaxf(mmax, base[p * kSlot + pairs * D + r]);
+        f32x4 acc[kHalf / 4];
+#pragma unroll
+        for (int i = 0; i < kHalf / 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float l = 0.f;
+        for (int p = 0; p < nparts; ++p) {
+            const float *slot = base + p * kSlot;
+            const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - mmax);
+            l += w * slot[pairs * (D + 1) + r];
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + half * kHalf);
+#pragma unroll
+            for (int i = 0; i < kHalf / 4; ++i) acc[i] += w * src[i];
+        }
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const int64_t obase = (row * hq + head) * D + half * kHalf;
+#pragma unroll
+        for (int i = 0; i < kHalf / 4; ++i) {
+            const f32x4 v = acc[i] * inv;
+            if constexpr (OUT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + 4 * i) =
+                    bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                           static_cast<__bf16>(v[3])};
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + 4 * i) = v;
+            }
+        }
+        if (lse && half == 0)
+            lse[static_cast<int64_t>(head) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+    }
 }
 
 int log2_of(int p)
@@ -952,7 +1256,12 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
     const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
     const u16 *vp = static_cast<const u16 *>(cfg.v_pool);
     const int log2P = log2_of(cfg.page_size);
-    if (cfg.page_size >= kBK)
+    if (cfg.page_size >= kBK && t.unit_rows * t.unit_heads <= kWaveRows)
+        hipLaunchKernelGGL((attn_decode_kernel<D, OUT_BF16>), grid, block, 0, stream, qh, kp, vp, cfg.num_pages,
+                           log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
+                           t.total_q_rows, cfg.num_q_heads, t.unit_rows, t.unit_heads, scale_log2, o, lse, parts,
+                           t.num_parts);
+    else if (cfg.page_size >= kBK)
         hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16>), grid, block, 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts, t.num_parts);
@@ -962,8 +1271,8 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse);
     if (t.num_merges > 0)
         hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges)), block, 0,
-                           stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_heads,
-                           t.total_q_rows, cfg.num_q_heads, o, lse);
+                           stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_rows,
+                           t.unit_heads, t.total_q_rows, cfg.num_q_heads, o, lse);
 }
 
 template <int D, int HPW>

@@ -29,16 +29,29 @@ constexpr int kMinRun = 16;
 
 // Shape of one attention work unit for a given GQA group size G: the
 // workgroup's four wavefronts cover `heads` query heads of one group times
-// `rows` query rows, one (head, 32-row block) per wavefront.
+// `rows` query rows, one (head, 32-row block) per wavefront. (The page size is
+// an argument so that kernels with other shapes can be chosen by it.)
 struct UnitShape {
     int rows;
     int heads;
 };
-inline UnitShape unit_shape(int G)
+inline UnitShape unit_shape(int G, int /*page_size*/)
 {
     int heads = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     return UnitShape{kWaveRows * (kWaves / heads), heads};
 }
+
+// Decode / small-chunk units: every new row of a segment (at most 32 / G)
+// for all G heads of its KV head, one (row, head) pair per MFMA column.
+inline bool decode_units(int G, int page_size, int max_new_rows)
+{
+    return page_size >= kKvTile && G <= kWaveRows && max_new_rows <= kWaveRows / G;
+}
+inline UnitShape decode_shape(int G) { return UnitShape{kWaveRows / G, G}; }
+// Workgroup slots of the decode kernel (one per CU) and the work units per
+// slot its split-KV policy aims at.
+constexpr int kDecodeSlots = 256;
+constexpr int kDecodeUnitsPerSlot = 4;
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_page_size(int p) { return p == 16 || p == 32 || p == 64 || p == 128 || p == 256; }

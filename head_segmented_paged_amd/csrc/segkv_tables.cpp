@@ -57,7 +57,10 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     if (static_cast<int64_t>(S) * hkv > std::numeric_limits<int32_t>::max())
         return fail(SEGKV_ERR_INVALID_ARG, "build_head_tables: too many segments");
 
-    const segkv::UnitShape shape = segkv::unit_shape(G);
+    int max_new = 0;
+    for (int32_t b = 0; b < S; ++b) max_new = std::max(max_new, in->new_len[b]);
+    const bool decode = segkv::decode_units(G, P, max_new);
+    const segkv::UnitShape shape = decode ? segkv::decode_shape(G) : segkv::unit_shape(G, P);
     std::vector<Seg> segs;
     segs.reserve(static_cast<size_t>(S) * hkv);
     int64_t q_rows = 0, pages = 0, units = 0, total_pairs = 0;
@@ -142,6 +145,12 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     if (P >= segkv::kKvTile && in->max_unit_tiles >= 0) {
         if (in->max_unit_tiles > 0) {
             max_run = in->max_unit_tiles;
+        } else if (decode) {
+            // Decode: a handful of long blocks; cut them into enough even runs
+            // for several units per workgroup slot.
+            const int64_t target = static_cast<int64_t>(segkv::kDecodeSlots) * segkv::kDecodeUnitsPerSlot;
+            max_run = std::max<int64_t>(segkv::kMinRun / 2, (total_tiles + target - 1) / target);
+            max_run += max_run & 1;
         } else {
             const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::kCohort;
             if (4 * longest * slots > 3 * total_tiles)
@@ -187,7 +196,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     out->unit_heads = shape.heads;
     out->num_merges = n_merges;
     out->num_parts = static_cast<int32_t>(n_parts);
-    out->workspace_bytes = n_parts * SEGKV_PART_BYTES(cfg.head_dim);
+    out->workspace_bytes = n_parts * SEGKV_PART_BYTES(shape.rows, shape.heads, cfg.head_dim);
     if (out->seg_cap < nseg || out->seq_cap < S || out->page_cap < pages || out->unit_cap < units ||
         out->merge_cap < n_merges)
         return fail(SEGKV_ERR_CAPACITY, "build_head_tables: buffers too small (need %d segments, %d sequences, "

@@ -27,9 +27,9 @@ UNIT_FIELDS = 8
 MERGE_FIELDS = 8
 
 
-def part_bytes(head_dim):
+def part_bytes(unit_rows, unit_heads, head_dim):
     """Workspace bytes per split-KV partial result (SEGKV_PART_BYTES)."""
-    return 512 * (head_dim + 2)
+    return 4 * unit_rows * unit_heads * (head_dim + 2)
 SEG_FIELD_NAMES = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len", "page_off")
 
 _P = ctypes.c_void_p
@@ -251,7 +251,8 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
         dt = SEGKV_DTYPE_BF16
     else:
         raise TypeError("o must be float32 or bfloat16")
-    need = int(dev_tables.struct.num_parts) * part_bytes(ctx.cfg.head_dim)
+    st = dev_tables.struct
+    need = int(st.num_parts) * part_bytes(st.unit_rows, st.unit_heads, ctx.cfg.head_dim)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

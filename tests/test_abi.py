@@ -135,7 +135,7 @@ def test_split_tables_need_a_workspace():
     host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
                                      max_unit_tiles=2)
     assert host["num_parts"] > 0 and host["num_merges"] > 0
-    assert host["workspace_bytes"] == host["num_parts"] * 512 * (w.d + 2)
+    assert host["workspace_bytes"] == host["num_parts"] * 4 * host["unit_rows"] * host["unit_heads"] * (w.d + 2)
     dt = S.segkv_dev_tables(1, 2, 3, host["num_segments"], host["num_units"], host["num_page_entries"],
                             host["total_q_rows"], host["unit_rows"], host["unit_heads"], 9, host["num_merges"],
                             host["num_parts"])

@@ -23,7 +23,8 @@ from oracle import paged as opaged
 from oracle import tables as otables
 from tests.common import adhoc
 from tests.gpu_helpers import GpuLayer, compare, device_pools, host_bits, sample_rows, say
-from workloads import LLAMA70B_32K, MISTRAL_8K, STACK64_128K, TINY, VARLEN_CHUNKED, layer_tensors, realize
+from workloads import (DECODE_32K, LLAMA70B_32K, MISTRAL_8K, STACK64_128K, TINY, VARLEN_CHUNKED, layer_tensors,
+                       realize)
 from workloads.gen import relabel_pages
 
 pytestmark = [pytest.mark.gpu,
@@ -127,6 +128,38 @@ def test_split_kv_all_rows(case):
     ob, _ = gl.attention(torch.bfloat16, with_lse=False)
     torch.cuda.synchronize()
     assert torch.equal(ob, o.to(torch.bfloat16))
+
+
+DECODE = [
+    # (hq, hkv, d, page, window, classes, seqs, longest run in tiles: 0 automatic)
+    (8, 2, 128, 64, 100, (0, 1), ((300, 1), (37, 5), (1000, 8), (5, 3)), 0),
+    (16, 2, 64, 128, 300, (1, 0), ((250, 2), (0, 4), (700, 1)), 3),
+    (8, 1, 128, 256, 40, (0,), ((700, 4), (3, 1)), 1),
+    (4, 4, 64, 64, 1, (1, 1, 0, 0), ((130, 7), (64, 32), (0, 1)), 2),
+    (32, 2, 128, 64, 2000, (1, 0), ((3000, 1), (64, 2)), 5),
+    (6, 3, 128, 64, 17, (0, 1, 0), ((129, 16), (500, 9)), 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_run{c[7]}")
+def test_decode_units_all_rows(case):
+    """A few new rows per sequence (at most 32 / G): decode units, one (row,
+    head) pair per MFMA column, with and without split runs."""
+    hq, hkv, d, page, window, classes, seqs, run = case
+    w = adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq + d + run)
+    o, lse, gl = run_case(w, max_unit_tiles=run)
+    G = hq // hkv
+    assert (gl.host["unit_rows"], gl.host["unit_heads"]) == (32 // G, G)
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+
+
+def test_decode_32k_all_rows():
+    """One decode step of 32 sequences at 32K (one new row each): every row of
+    every head against the oracle, split-KV runs merged."""
+    o, lse, gl = run_case(DECODE_32K)
+    assert gl.host["num_parts"] > 0
 
 
 def test_mistral_8k_sampled():

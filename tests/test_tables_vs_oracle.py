@@ -69,7 +69,9 @@ def _check_work(lib, w):
     G = w.hq // w.hkv
     work = lib["work"]
     rows, heads = lib["unit_rows"], lib["unit_heads"]
-    assert rows * heads == 128
+    decode = w.page >= 64 and G <= 32 and int(lib["n_q"].max()) <= 32 // G
+    prefill_heads = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    assert (heads, rows) == ((G, 32 // G) if decode else (prefill_heads, 128 // prefill_heads))
     assert (work[:, 6:] == 0).all()
     _check_order(work)
     # blocks: every (segment, head, row) in exactly one block; a block's units
@@ -107,7 +109,7 @@ def _check_work(lib, w):
             assert parts == list(range(m[3], m[3] + m[4]))
             seen_parts += parts
     assert sorted(seen_parts) == list(range(lib["num_parts"]))
-    assert lib["workspace_bytes"] == lib["num_parts"] * 512 * (w.d + 2)
+    assert lib["workspace_bytes"] == lib["num_parts"] * 4 * rows * heads * (w.d + 2)
 
 
 @pytest.mark.parametrize("w", [x for x in ALL if x.layers == 1], ids=lambda w: w.name)
@@ -127,7 +129,7 @@ def test_stack_all_layers():
         if layer in (0, 8, 63):
             work = lib["work"]
             _check_order(work)
-            assert len(work) == 8 * (131072 // 32)
+            assert len(work) == 8 * (131072 // lib["unit_rows"])
 
 
 SMALL = [((0, 1),), ((0, 17),), ((5, 30),), ((37, 100),), ((0, 100), (37, 15), (5, 2)),
@@ -160,16 +162,18 @@ def test_automatic_split_policy():
     block (128 tiles) exceeds 3/4 of the mean load per workgroup slot."""
     by = {x.name: x for x in ALL}
     for name, expect in (("mistral7b_like_l8192", True), ("llama70b_like_l32768", False),
-                         ("varlen16_chunk2048", False), ("tiny_gqa2_l512", False)):
+                         ("varlen16_chunk2048", False), ("tiny_gqa2_l512", False), ("decode32_l32768", True)):
         w = by[name]
         r = realize(w)
         ctx = _ctx(w, r.num_pages)
         lib = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0],
                                         r.page_of[0])
         assert (lib["num_parts"] > 0) == expect, name
-        if expect:
+        if expect and lib["unit_rows"] * lib["unit_heads"] == 128:
             total = int(lib["work"][:, 3].sum())
             assert lib["work"][:, 3].max() <= max(16, -(-total // 1024)) + 1
+        if expect and lib["unit_rows"] * lib["unit_heads"] < 128:      # decode: >= 4 units per CU
+            assert len(lib["work"]) >= 4 * 256 * 0.9
         never = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0],
                                           r.page_of[0], max_unit_tiles=-1)
         assert never["num_parts"] == 0

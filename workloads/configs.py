@@ -86,5 +86,15 @@ VARLEN_CHUNKED = Workload(
          "32 q / 8 kv, D 128, 1 of 8 kv heads global, W 1024; P 64; one shared pool",
 )
 
-ALL = (TINY, MISTRAL_8K, LLAMA70B_32K, STACK64_128K, VARLEN_CHUNKED)
+DECODE_32K = Workload(
+    name="decode32_l32768",
+    layers=1, hq=64, hkv=8, d=128, page=64, window=2048,
+    class_rule=("count", 1),
+    seq_rule=("fixed", tuple((32767, 1) for _ in range(32))),
+    seed=1006,
+    note="one decode step of 32 concurrent sequences at 32K: 32767 cached tokens and 1 new token each; "
+         "64 q / 8 kv, D 128, 1 of 8 kv heads global, W 2048; P 64",
+)
+
+ALL = (TINY, MISTRAL_8K, LLAMA70B_32K, STACK64_128K, VARLEN_CHUNKED, DECODE_32K)
 BY_NAME = {w.name: w for w in ALL}
