@@ -227,6 +227,10 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         out->cu_seqlens_k[s + 1] = static_cast<int32_t>(k_acc);
         out->cu_pages[s + 1] = sg.page_off + sg.n_pages;
         out->pairs[s] = sg.pairs;
+        if (out->retain_lp) {
+            const int64_t T = static_cast<int64_t>(sg.q_pos0) + sg.n_q;
+            out->retain_lp[s] = sg.window == 0 ? 0 : static_cast<int32_t>(std::max<int64_t>(0, T - sg.window + 1) / P);
+        }
         const int32_t b = s / hkv;
         const int32_t *row = in->page_of + static_cast<int64_t>(s) * in->max_lp;
         (void)b;

@@ -54,7 +54,7 @@ class segkv_tables(ctypes.Structure):
                 ("seg_desc", _P), ("cu_seqlens_q", _P), ("cu_seqlens_k", _P), ("cu_pages", _P),
                 ("page_list", _P), ("pairs", _P), ("work", _P),
                 ("merge_cap", _i32), ("num_merges", _i32), ("num_parts", _i32), ("workspace_bytes", _i64),
-                ("merge", _P)]
+                ("merge", _P), ("retain_lp", _P)]
 
 
 class segkv_dev_tables(ctypes.Structure):
@@ -197,6 +197,7 @@ def segkv_build_head_tables(ctx, cached_len, new_len, head_class, window, page_o
         "pairs": np.zeros(S, np.int64),
         "work": np.zeros((max(out.num_units, 1), UNIT_FIELDS), np.int32),
         "merge": np.zeros((max(out.num_merges, 1), MERGE_FIELDS), np.int32),
+        "retain_lp": np.zeros(S, np.int32),
     }
     out2 = segkv_tables(S, c.shape[0], bufs["page_list"].shape[0], bufs["work"].shape[0])
     out2.merge_cap = bufs["merge"].shape[0]

@@ -106,9 +106,11 @@ enum {
     SEGKV_MERGE_FIELDS = 8  /* fields 5 .. 7 are zero */
 };
 
-/* Workspace bytes per partial result: 128 (query row, head) pairs, each with
- * head_dim unnormalised fp32 outputs plus its running maximum and sum. */
-#define SEGKV_PART_BYTES(head_dim) (512 * ((int64_t)(head_dim) + 2))
+/* Workspace bytes per partial result: the unit's unit_rows * unit_heads
+ * (query row, head) pairs, each with head_dim unnormalised fp32 outputs plus
+ * its running maximum and sum. */
+#define SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) \
+    (4 * (int64_t)(unit_rows) * (int64_t)(unit_heads) * ((int64_t)(head_dim) + 2))
 
 typedef struct segkv_ctx segkv_ctx;
 
@@ -177,6 +179,11 @@ int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new
  * ... (the workgroups one XCD receives) hold neighbours in (segment, row)
  * order, which then share that XCD's L2.
  *
+ * retain_lp [num_segments]: the first logical page a later query of the
+ * segment can still see, so the caller may free the pages before it once
+ * this step is done: 0 for a global head; floor(max(0, T_b - W + 1) / P) for
+ * a local head (the next query, at position T_b, sees keys >= T_b - W + 1).
+ *
  * Split-KV (page_size >= 64 only). With max_unit_tiles == 0 the builder splits
  * when the longest block would visit more than 3/4 of the mean tiles per
  * workgroup slot (512 slots): then every block longer than
@@ -184,7 +191,8 @@ int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new
  * max_unit_tiles > 0 cuts every block longer than that; < 0 never splits.
  * A split block's runs become separate units with workspace slots, and one
  * merge entry per block; segkv_attn_prefill then needs workspace_bytes =
- * num_parts * SEGKV_PART_BYTES(head_dim) of device workspace.
+ * num_parts * SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) of device
+ * workspace.
  */
 typedef struct segkv_table_inputs {
     int32_t num_seqs;
@@ -223,8 +231,9 @@ typedef struct segkv_tables {
     int32_t merge_cap;          /* merge entries (set by the caller) */
     int32_t num_merges;
     int32_t num_parts;          /* workspace slots */
-    int64_t workspace_bytes;    /* num_parts * SEGKV_PART_BYTES(head_dim) */
+    int64_t workspace_bytes;    /* num_parts * SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) */
     int32_t *merge;             /* [merge_cap][SEGKV_MERGE_FIELDS] */
+    int32_t *retain_lp;         /* [seg_cap] (appended), or NULL to skip */
 } segkv_tables;
 
 int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_inputs *in, segkv_tables *out);
@@ -253,7 +262,8 @@ typedef struct segkv_dev_tables {
  *   lse : device fp32 [hq][total_q_rows] natural-log sum of exp of the scaled
  *         scores, or NULL
  *   softmax_scale : multiplies q.k; <= 0 selects 1/sqrt(head_dim)
- *   workspace : device memory of at least t->num_parts * SEGKV_PART_BYTES(head_dim)
+ *   workspace : device memory of at least
+ *               t->num_parts * SEGKV_PART_BYTES(t->unit_rows, t->unit_heads, head_dim)
  *               bytes (caller-owned; may be NULL when num_parts == 0). Its
  *               contents need no initialisation and are scratch afterwards;
  *               calls that share a workspace must not overlap.

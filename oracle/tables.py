@@ -64,7 +64,7 @@ def build_tables(cached_len, new_len, head_class, window, page_of, hq, hkv, page
     cu_q = [0]
     q_row0, n_q, q_pos0, kv_head, q_head0 = [], [], [], [], []
     win_out, k_pos0, k_len = [], [], []
-    cu_k, cu_pages, page_list, pairs = [0], [0], [], []
+    cu_k, cu_pages, page_list, pairs, retain = [0], [0], [], [], []
 
     for b in range(nseq):
         c = int(cached_len[b])
@@ -110,6 +110,9 @@ def build_tables(cached_len, new_len, head_class, window, page_of, hq, hkv, page
             cu_k.append(cu_k[-1] + T - first_pos)
             cu_pages.append(len(page_list))
             pairs.append(G * int(count.sum()))
+            # pages a later query (position >= T) can still see: a local head's
+            # next query starts its window at T - W + 1, a global head sees all
+            retain.append(0 if is_global else max(0, T - W + 1) // page)
         cu_q.append(cu_q[-1] + n)
 
     i32 = lambda x: np.asarray(x, dtype=np.int32)  # noqa: E731
@@ -119,5 +122,6 @@ def build_tables(cached_len, new_len, head_class, window, page_of, hq, hkv, page
         "k_pos0": i32(k_pos0), "k_len": i32(k_len),
         "cu_seqlens_q": i32(cu_q), "cu_seqlens_k": i32(cu_k), "cu_pages": i32(cu_pages),
         "page_list": i32(page_list), "pairs": np.asarray(pairs, dtype=np.int64),
+        "retain_lp": i32(retain),
         "G": G, "page": page, "hq": hq, "hkv": hkv,
     }

@@ -105,6 +105,32 @@ def test_workload_totals_match_closed_forms(w):
                 s += 1
 
 
+@pytest.mark.parametrize("W", [1, 5, 16, 17, 40])
+@pytest.mark.parametrize("page", [1, 4, 16])
+def test_retain_from_page_against_the_mask(W, page):
+    """retain_lp: pages before it hold no key a later query can see; the page
+    itself holds one (checked against the explicit mask of a longer sequence
+    whose first c + n rows are this step)."""
+    seqs = ((0, 1), (0, 23), (9, 7), (30, 2), (64, 64))
+    w = adhoc(hq=4, hkv=2, d=8, page=page, window=W, classes=(1, 0), seqs=seqs)
+    r = realize(w)
+    t = build_tables(r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
+                     w.hq, w.hkv, w.page, r.num_pages)
+    s = 0
+    for b, (c, n) in enumerate(seqs):
+        T = c + n
+        for g in range(w.hkv):
+            glob = bool(r.head_class[0, g])
+            # rows T .. T + 2W + page of a continuation: the queries still to come
+            future = bruteforce.visibility_mask(T, 2 * W + page + 1, glob, W)   # [rows][T + rows]
+            seen = np.flatnonzero(future[:, :T].any(axis=0))
+            first_needed = int(seen.min()) if seen.size else T
+            lp = int(t["retain_lp"][s])
+            assert lp * page <= first_needed
+            assert first_needed < (lp + 1) * page or (glob and lp == 0)
+            s += 1
+
+
 def test_printed_pair_counts():
     """Pair totals of the three single-sequence workloads, from the closed forms
     written out by hand: global q-head L(L+1)/2, local W(W+1)/2 + (L-W)W."""

@@ -11,7 +11,7 @@ from tests.common import adhoc
 from workloads import ALL, STACK64_128K, realize
 
 FIELDS = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len",
-          "cu_seqlens_q", "cu_seqlens_k", "cu_pages", "page_list", "pairs")
+          "cu_seqlens_q", "cu_seqlens_k", "cu_pages", "page_list", "pairs", "retain_lp")
 
 
 class FakeDev:
