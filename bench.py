@@ -239,6 +239,37 @@ def cpu_baseline(res, target_s=12.0):
     }
 
 
+def rope_bench(torch, n_pages, steps, warmup, P=64, D=128):
+    """RoPE re-alignment of n_pages whole K pages (each turned by its own
+    delta), timed with HIP events on the launch stream. Bytes = every K page
+    read and written once."""
+    import head_segmented_paged_amd as H
+    k = torch.randn((n_pages, P, D), device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros((1, D, P), device="cuda", dtype=torch.bfloat16)
+    ctx = H.segkv_create(k, v, 32, 8, D, P, num_pages=n_pages)
+    rng = np.random.Generator(np.random.PCG64(11))
+    ent = np.stack([np.arange(n_pages), np.zeros(n_pages), np.full(n_pages, P),
+                    rng.integers(-65536, 65536, n_pages)], 1).astype(np.int32)
+    ent = torch.from_numpy(ent).cuda()
+    for _ in range(warmup):
+        H.segkv_rope_realign(ctx, ent)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        H.segkv_rope_realign(ctx, ent)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    gbs = 2.0 * n_pages * P * D * 2 / (ms / 1e3) / 1e9
+    return {"metric": "RoPE re-alignment of reused K pages", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"rope_realign_{n_pages}pages_p{P}_d{D}", "pages": n_pages},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+
+
 def run_secondary(name, steps=5, warmup=2):
     from workloads import BY_NAME
     res = Resident(BY_NAME[name])
@@ -267,6 +298,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
+    ap.add_argument("--rope-pages", type=int, default=0, metavar="N",
+                    help="only time the RoPE re-alignment of N reused K pages (P 64, D 128), in GB/s")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
@@ -285,6 +318,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.rope_pages:
+        print(json.dumps(rope_bench(torch, args.rope_pages, args.steps, args.warmup)), flush=True)
         return
     w = BY_NAME[args.workload]
     log(f"[bench] setting up {w.name} ({w.layers} layers)")

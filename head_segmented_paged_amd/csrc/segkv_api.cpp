@@ -84,6 +84,19 @@ extern "C" int segkv_gather_pages(const segkv_ctx *ctx, const int32_t *page_ids,
     return segkv::launch_gather_pages(ctx->cfg, page_ids, n, k_out, v_out, stream);
 }
 
+extern "C" int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, int64_t n, float rope_base,
+                                  void *stream)
+{
+    segkv::clear_error();
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "rope_realign: null context");
+    if (n < 0 || n > 0x7fffffff) return fail(SEGKV_ERR_INVALID_ARG, "rope_realign: entry count out of range");
+    if (!(rope_base > 1.0f) || !std::isfinite(rope_base))
+        return fail(SEGKV_ERR_INVALID_ARG, "rope_realign: rope_base must be a finite value > 1");
+    if (n == 0) return SEGKV_OK;
+    if (!entries) return fail(SEGKV_ERR_INVALID_ARG, "rope_realign: null entries");
+    return segkv::launch_rope_realign(ctx->cfg, entries, n, rope_base, stream);
+}
+
 extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
                                   int32_t o_dtype, float *lse, float softmax_scale, void *workspace,
                                   int64_t workspace_bytes, void *stream)

@@ -63,6 +63,7 @@ int launch_write_pages(const segkv_config &cfg, const void *k_new, const void *v
                        int32_t max_lp, int32_t max_rows_per_seq, void *stream);
 int launch_gather_pages(const segkv_config &cfg, const int32_t *page_ids, int64_t n, void *k_out, void *v_out,
                         void *stream);
+int launch_rope_realign(const segkv_config &cfg, const int32_t *entries, int64_t n, float rope_base, void *stream);
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
                         int32_t o_dtype, float *lse, float scale_log2, void *workspace, void *stream);
 

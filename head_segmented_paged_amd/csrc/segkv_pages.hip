@@ -1,4 +1,5 @@
-// Paged KV write (BUILDSTATE) and page read-back kernels for gfx950.
+// Paged KV write (BUILDSTATE), RoPE re-alignment of reused K pages and page
+// read-back kernels for gfx950.
 //
 // Pool layout: K page = bf16 [P][D] (slot-major), V page = bf16 [D][P]
 // (dimension-major, the key index innermost). Both are one contiguous block
@@ -8,6 +9,8 @@
 // V rows are staged through LDS and written back transposed, each lane
 // storing 8 consecutive slots of one dimension.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "segkv_internal.h"
 
@@ -114,6 +117,51 @@ int log2_of(int p)
     return l;
 }
 
+// RoPE re-alignment (RedKnot summary page, "Elastic Sparsity": recovery starts
+// by aligning reused K to its new positions). A K row encoded with rotary
+// angles p * theta_i becomes the row encoded at p + delta by one more rotation
+// of each pair (i, i + D/2) by delta * theta_i. One workgroup per entry (page,
+// slot range, delta): the D/2 angles are reduced and evaluated in fp64 once,
+// then every slot rotates in fp32 and rounds to bf16 (nearest even).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(kThreads) void rope_realign_kernel(const int32_t *__restrict__ entries, u16 *k_pool,
+                                                                int64_t num_pages, int32_t D, int32_t log2P,
+                                                                double log2_base)
+{
+    __shared__ float cs[2][64];   // cos, sin per frequency (D <= 128)
+    const int32_t *ent = entries + static_cast<int64_t>(blockIdx.x) * 4;
+    const int32_t page = ent[0], slot0 = ent[1], nslots = ent[2], delta = ent[3];
+    const int32_t P = 1 << log2P, H = D / 2;
+    if (page < 0 || page >= num_pages || slot0 < 0 || slot0 >= P || nslots <= 0) return;
+    const int32_t s_end = slot0 + min(nslots, P - slot0);
+    if (threadIdx.x < H) {
+        const double theta = exp2(-log2_base * (2.0 * threadIdx.x / D));
+        const double ang = static_cast<double>(delta) * theta;
+        cs[0][threadIdx.x] = static_cast<float>(cos(ang));
+        cs[1][threadIdx.x] = static_cast<float>(sin(ang));
+    }
+    __syncthreads();
+    const int32_t per_slot = H / 8;   // threads per slot: 8 pairs each
+    u16 *base = k_pool + (static_cast<int64_t>(page) << log2P) * D;
+    for (int32_t c = threadIdx.x; c < (s_end - slot0) * per_slot; c += kThreads) {
+        const int32_t s = slot0 + c / per_slot, i0 = (c % per_slot) * 8;
+        bf16x8 *px = reinterpret_cast<bf16x8 *>(base + static_cast<int64_t>(s) * D + i0);
+        bf16x8 *py = reinterpret_cast<bf16x8 *>(base + static_cast<int64_t>(s) * D + H + i0);
+        const bf16x8 x = *px, y = *py;
+        bf16x8 xo, yo;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float c0 = cs[0][i0 + k], s0 = cs[1][i0 + k];
+            const float xf = static_cast<float>(x[k]), yf = static_cast<float>(y[k]);
+            xo[k] = static_cast<__bf16>(xf * c0 - yf * s0);
+            yo[k] = static_cast<__bf16>(xf * s0 + yf * c0);
+        }
+        *px = xo;
+        *py = yo;
+    }
+}
+
 int check_launch(const char *what)
 {
     hipError_t err = hipGetLastError();
@@ -150,6 +198,14 @@ int launch_gather_pages(const segkv_config &cfg, const int32_t *page_ids, int64_
                        static_cast<const u16 *>(cfg.v_pool), cfg.num_pages, cfg.head_dim, log2_of(cfg.page_size),
                        static_cast<u16 *>(k_out), static_cast<u16 *>(v_out));
     return check_launch("gather_pages");
+}
+
+int launch_rope_realign(const segkv_config &cfg, const int32_t *entries, int64_t n, float rope_base, void *stream)
+{
+    hipLaunchKernelGGL(rope_realign_kernel, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), entries, static_cast<u16 *>(cfg.k_pool), cfg.num_pages,
+                       cfg.head_dim, log2_of(cfg.page_size), std::log2(static_cast<double>(rope_base)));
+    return check_launch("rope_realign");
 }
 
 }  // namespace segkv

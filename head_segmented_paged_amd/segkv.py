@@ -71,7 +71,11 @@ class SegKVError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m head_segmented_paged_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python head_segmented_paged_amd/build.py`")
+    # torch brings its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Load it first, so the library binds to that one copy: with two runtimes
+    # in one process the library's would see no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "segkv_create": ([ctypes.POINTER(segkv_config), ctypes.POINTER(_P)], ctypes.c_int),
@@ -82,6 +86,7 @@ def _load():
         "segkv_attn_prefill": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P, _i64,
                                 _P], ctypes.c_int),
         "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
+        "segkv_rope_realign": ([_P, _P, _i64, ctypes.c_float, _P], ctypes.c_int),
         "segkv_last_error": ([], ctypes.c_char_p),
         "segkv_version": ([], ctypes.c_char_p),
     }
@@ -94,7 +99,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
-            "segkv_attn_prefill", "segkv_gather_pages", "segkv_last_error", "segkv_version")
+            "segkv_attn_prefill", "segkv_gather_pages", "segkv_rope_realign", "segkv_last_error", "segkv_version")
 
 
 def segkv_last_error() -> str:
@@ -259,6 +264,11 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
                                    _ptr(lse), float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segkv_rope_realign(ctx, entries, rope_base=10000.0, stream=None):
+    """entries: device int32 [n][4] = (page, slot0, nslots, delta); rotates those K slots in place."""
+    _check(_lib.segkv_rope_realign(ctx.handle, _ptr(entries), entries.shape[0], float(rope_base), _stream(stream)))
 
 
 def segkv_gather_pages(ctx, page_ids, k_out, v_out, stream=None):

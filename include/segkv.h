@@ -280,6 +280,24 @@ int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const vo
                        int64_t workspace_bytes, void *stream);
 
 /*
+ * RoPE re-alignment of reused K pages (position-independent KV reuse; RedKnot
+ * summary page, "Elastic Sparsity": recovery begins with RoPE position
+ * alignment). entries: device int32 [n][4] = {page, slot0, nslots, delta}.
+ * Slots slot0 .. slot0 + nslots - 1 (cut at the page end) of K page `page`
+ * hold rows encoded with rotary angles at positions p; afterwards they hold
+ * the rows encoded at p + delta. Rotary angles add, so each pair of
+ * dimensions (i, i + D/2), i < D/2, is rotated by a = delta * theta_i with
+ * theta_i = rope_base^(-2 i / D):
+ *     x' = x cos a - y sin a,   y' = x sin a + y cos a
+ * (pairing and base follow the rotate-half convention of the Llama family;
+ * the pages fix neither). The angles are evaluated in fp64, the rotation in
+ * fp32, the result rounded to bf16 (nearest even). V pages are position-free
+ * and untouched. An entry whose page id is outside [0, num_pages) or whose
+ * slot range is empty is skipped; entries that overlap race. rope_base > 1.
+ */
+int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, int64_t n, float rope_base, void *stream);
+
+/*
  * Read pages back in a dense layout (tests, debugging):
  *   page_ids : device int32 [n]
  *   k_out, v_out : device bf16 [n][page_size][head_dim] each (V un-transposed)

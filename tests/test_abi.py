@@ -155,6 +155,18 @@ def test_split_tables_need_a_workspace():
     assert rc == S.SEGKV_ERR_UNSUPPORTED
 
 
+def test_rope_realign_validates_before_launch():
+    ctx = _ctx(d=128, p=64)
+    rc = S._lib.segkv_rope_realign(ctx.handle, None, 3, 10000.0, None)
+    assert rc == S.SEGKV_ERR_INVALID_ARG and "entries" in H.segkv_last_error()
+    rc = S._lib.segkv_rope_realign(ctx.handle, 8, -1, 10000.0, None)
+    assert rc == S.SEGKV_ERR_INVALID_ARG
+    rc = S._lib.segkv_rope_realign(ctx.handle, 8, 3, 1.0, None)
+    assert rc == S.SEGKV_ERR_INVALID_ARG and "rope_base" in H.segkv_last_error()
+    assert S._lib.segkv_rope_realign(ctx.handle, None, 0, 10000.0, None) == S.SEGKV_OK   # nothing to do
+    assert S._lib.segkv_rope_realign(None, 8, 3, 10000.0, None) == S.SEGKV_ERR_INVALID_ARG
+
+
 def test_write_and_gather_validate_before_launch():
     ctx = _ctx()
     rc = S._lib.segkv_write_pages(ctx.handle, None, 2, 10, 3, 4, 5, 1, 4, 16, None)
