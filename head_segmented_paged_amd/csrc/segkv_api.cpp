@@ -84,6 +84,26 @@ extern "C" int segkv_gather_pages(const segkv_ctx *ctx, const int32_t *page_ids,
     return segkv::launch_gather_pages(ctx->cfg, page_ids, n, k_out, v_out, stream);
 }
 
+extern "C" int segkv_attn_mass(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, const float *lse,
+                               float softmax_scale, float *mass, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx || !t) return fail(SEGKV_ERR_INVALID_ARG, "attn_mass: null argument");
+    const segkv_config &cfg = ctx->cfg;
+    if (cfg.page_size < 64) return fail(SEGKV_ERR_UNSUPPORTED, "attn_mass: needs page_size >= 64");
+    const segkv::UnitShape shape = segkv::unit_shape(cfg.num_q_heads / cfg.num_kv_heads, cfg.page_size);
+    if (t->unit_rows != shape.rows || t->unit_heads != shape.heads)
+        return fail(SEGKV_ERR_UNSUPPORTED, "attn_mass: needs prefill units of %d rows x %d heads (tables have "
+                    "%d x %d)", shape.rows, shape.heads, t->unit_rows, t->unit_heads);
+    if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0)
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_mass: negative table size");
+    if (t->total_q_rows == 0) return SEGKV_OK;
+    if (!mass || !lse || !q || (t->num_units > 0 && (!t->seg_desc || !t->page_list || !t->work)))
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_mass: null pointer");
+    float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
+    return segkv::launch_attn_mass(cfg, *t, q, lse, scale * 1.44269504088896340736f, mass, stream);
+}
+
 extern "C" int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, int64_t n, float rope_base,
                                   void *stream)
 {

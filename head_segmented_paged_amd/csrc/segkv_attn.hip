@@ -37,6 +37,7 @@
 // never reach P.V.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "segkv_internal.h"
@@ -1181,6 +1182,179 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
         lse[static_cast<int64_t>(hd) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
 }
 
+// Attention mass of the step's new tokens (RedKnot summary page, "Sparse
+// FFN": the tokens with the highest attention scores get the dense FFN). A
+// second pass over the same units, after the attention has produced the LSE:
+// S = Q . K^T with Q as the A operand, so each lane owns one key column and
+// its accumulator registers are query rows; p = exp(s - lse) then sums over
+// the queries inside the lane, plus one exchange between the two 32-lane
+// halves. Each wave adds its 64 column sums to mass[] with float atomics
+// (several heads, row blocks and KV heads reach the same token). Only K is
+// staged; keys before the step (cached tokens) are not visited.
+template <int D, int HPW>
+__global__ __launch_bounds__(kThreads, 2) void attn_mass_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ kpool, int64_t num_pages, int log2P,
+    const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list, int64_t num_page_entries,
+    const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows, int32_t hq, float scale_log2,
+    const float *__restrict__ lse, float *__restrict__ mass)
+{
+    using T = DmaTile<D>;
+    constexpr int kRowBlocks = kWaves / HPW;
+    constexpr int kUnitRows = kWaveRows * kRowBlocks;
+    constexpr int kSteps = D / 16;
+    __shared__ __attribute__((aligned(1024))) char kst0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char kst1[T::kBytes];
+
+    const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
+    const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
+    const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
+    const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
+    if (seg < 0 || seg >= num_segments) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1 || q_pos0 < k_pos0)
+        return;
+    int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
+    if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
+    const int32_t *pages = page_list + page_off;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const int head = head0 + wave % HPW;
+    const int wrow0 = row0 + (wave / HPW) * kWaveRows;
+
+    const int unit_end = min(row0 + kUnitRows, n_q);
+    const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
+    const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
+    // the unit's run, from the first tile holding a new token
+    const int tile_beg = max(max((lo_pos - k_pos0) / kBK, run0), (q_pos0 - k_pos0) / kBK);
+    const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
+    const int key_end = k_pos0 + k_len;   // one past the last stored key (the step's last token)
+
+    const bool wave_valid = wrow0 < n_q && head < hq;
+    const int wrow_end = min(wrow0 + kWaveRows, n_q);
+    const int wp_lo = q_pos0 + wrow0, wp_hi = q_pos0 + max(wrow_end, wrow0 + 1) - 1;
+
+    // A operand: query row `col`, 8 dims per k-step (the same registers as the
+    // B operand of the attention kernel).
+    bf16x8 qreg[kSteps];
+    {
+        const int my_t = min(wrow0 + col, n_q - 1);
+        const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
+        const bool can_load = wave_valid && my_row < total_q_rows;
+        const u16 *qp = q + (my_row * hq + min(head, hq - 1)) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+            qreg[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    // The query rows of this lane's accumulator registers: e -> 8 (e / 4) +
+    // 4 half + e % 4. Their LSE in log2 units (+inf: row absent, weight 0).
+    float lse2[16];
+    int qpos[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int t = wrow0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool ok = wave_valid && t < n_q && static_cast<int64_t>(q_row0) + t < total_q_rows;
+        lse2[e] = ok ? lse[static_cast<int64_t>(head) * total_q_rows + q_row0 + t] * 1.44269504088896340736f
+                     : __builtin_inff();
+        qpos[e] = q_pos0 + t;
+    }
+
+    int win = ((tile_beg * kBK) >> log2P) >> 6;
+    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
+    int win_cur = load_window(win), win_next = load_window(win + 1);
+    auto tile_page = [&](int jt) {
+        const int lp = (jt * kBK) >> log2P;
+        if ((lp >> 6) != win) {
+            win = lp >> 6;
+            win_cur = win_next;
+            win_next = load_window(win + 1);
+        }
+        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
+        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    };
+    unsigned kdma[T::kInstr];
+#pragma unroll
+    for (int i = 0; i < T::kInstr; ++i) {
+        const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
+        const int r = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(r);
+        kdma[i] = static_cast<unsigned>(r * T::kRowBytes + c * 16);
+    }
+    auto dma_k = [&](char *dst, int jt) {
+        const int page = tile_page(jt);
+        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
+        const int64_t pg = page >= 0 ? page : 0;
+        const __amdgpu_buffer_rsrc_t rk =
+            page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
+#pragma unroll
+        for (int i = 0; i < T::kInstr; ++i)
+            dma16(rk, dst + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+    };
+
+    auto compute = [&](const char *kt, int jt) {
+        const int kp0 = k_pos0 + jt * kBK;
+        const bool full = kp0 >= q_pos0 && kp0 + kBK <= key_end && kp0 + kBK - 1 <= wp_lo &&
+                          (window == 0 || kp0 >= wp_hi - window + 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 32 * h + col;   // key row of this lane's column
+            f32x16 sacc = {};
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const bf16x8 b =
+                    *reinterpret_cast<const bf16x8 *>(kt + r * T::kRowBytes + (((2 * s + half) ^ kswz<D>(r)) << 4));
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[s], b, sacc, 0, 0, 0);
+            }
+            const int kpos = kp0 + r;
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], scale_log2, -lse2[e]));
+                if (!full) {
+                    const bool vis = kpos <= qpos[e] && (window == 0 || qpos[e] - kpos < window) &&
+                                     kpos >= q_pos0 && kpos < key_end;
+                    p = vis ? p : 0.f;
+                }
+                acc += p;
+            }
+            float lo, hi;
+            swap_halves(acc, lo, hi);
+            const float tot = lo + hi;
+            if (half == 0 && wave_valid && kpos >= q_pos0 && kpos < key_end)
+                atomicAdd(mass + q_row0 + (kpos - q_pos0), tot);
+        }
+    };
+
+    if (tile_beg < tile_end) {
+        dma_k(kst0, tile_beg);
+        __syncthreads();
+        int jt = tile_beg;
+        auto iteration = [&](int j, char *cur, char *nxt) {
+            if (j + 1 < tile_end) dma_k(nxt, j + 1);
+            compute(cur, j);
+            __syncthreads();
+        };
+        for (; jt + 1 < tile_end; jt += 2) {
+            iteration(jt, kst0, kst1);
+            iteration(jt + 1, kst1, kst0);
+        }
+        if (jt < tile_end) iteration(jt, kst0, kst1);
+    }
+}
+
+__global__ void fill_zero_kernel(float *__restrict__ x, int64_t n)
+{
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        x[i] = 0.f;
+}
+
 // Merge pass for split blocks (split-KV): one workgroup per merge entry, two
 // lanes per (query row, head) pair, each lane half of the head dim. The runs'
 // partial results combine exactly as blocks of one online softmax:
@@ -1296,7 +1470,44 @@ void launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void
     }
 }
 
+template <int D>
+void launch_mass(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, const float *lse,
+                 float scale_log2, float *mass, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(t.num_units)), block(kThreads);
+    const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
+    const int log2P = log2_of(cfg.page_size);
+#define SEGKV_MASS(HPW)                                                                                       \
+    hipLaunchKernelGGL((attn_mass_kernel<D, HPW>), grid, block, 0, stream, qh, kp, cfg.num_pages, log2P,         \
+                       t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments, t.total_q_rows,       \
+                       cfg.num_q_heads, scale_log2, lse, mass)
+    switch (t.unit_heads) {
+    case 4: SEGKV_MASS(4); break;
+    case 2: SEGKV_MASS(2); break;
+    default: SEGKV_MASS(1); break;
+    }
+#undef SEGKV_MASS
+}
+
 }  // namespace
+
+int launch_attn_mass(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, const float *lse,
+                     float scale_log2, float *mass, void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = t.total_q_rows;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
+    if (n > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, s, mass, n);
+    if (t.num_units > 0) {
+        if (cfg.head_dim == 128)
+            launch_mass<128>(cfg, t, q, lse, scale_log2, mass, s);
+        else
+            launch_mass<64>(cfg, t, q, lse, scale_log2, mass, s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_mass: %s", hipGetErrorString(err));
+    return SEGKV_OK;
+}
 
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
                         int32_t o_dtype, float *lse, float scale_log2, void *workspace, void *stream)

@@ -87,6 +87,7 @@ def _load():
                                 _P], ctypes.c_int),
         "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
         "segkv_rope_realign": ([_P, _P, _i64, ctypes.c_float, _P], ctypes.c_int),
+        "segkv_attn_mass": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
         "segkv_last_error": ([], ctypes.c_char_p),
         "segkv_version": ([], ctypes.c_char_p),
     }
@@ -99,7 +100,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
-            "segkv_attn_prefill", "segkv_gather_pages", "segkv_rope_realign", "segkv_last_error", "segkv_version")
+            "segkv_attn_prefill", "segkv_attn_mass", "segkv_gather_pages", "segkv_rope_realign", "segkv_last_error",
+            "segkv_version")
 
 
 def segkv_last_error() -> str:
@@ -264,6 +266,12 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
                                    _ptr(lse), float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segkv_attn_mass(ctx, dev_tables, q, lse, mass, softmax_scale=0.0, stream=None):
+    """Attention mass of the new tokens: mass fp32 [rows], lse fp32 [hq][rows] from segkv_attn_prefill."""
+    _check(_lib.segkv_attn_mass(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(lse),
+                                float(softmax_scale), _ptr(mass), _stream(stream)))
 
 
 def segkv_rope_realign(ctx, entries, rope_base=10000.0, stream=None):

@@ -280,6 +280,26 @@ int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const vo
                        int64_t workspace_bytes, void *stream);
 
 /*
+ * Attention mass of the step's new tokens (RedKnot summary page, "Sparse
+ * FFN": only the tokens with the highest attention scores run the dense
+ * FFN; this is the score). Run after segkv_attn_prefill on the same tables
+ * and inputs, with the LSE it wrote:
+ *   mass[q_row0(b) + t] = sum over query heads h and query rows t' of
+ *                         sequence b that see position c_b + t of
+ *                         exp(scale * q[t', h] . k[c_b + t] - lse[h][t'])
+ *   q    : device bf16 [total_q_rows][hq][head_dim] (as for the attention)
+ *   lse  : device fp32 [hq][total_q_rows] from segkv_attn_prefill
+ *   mass : device fp32 [total_q_rows], overwritten (cleared first, then
+ *          accumulated with float atomics: the summation order varies)
+ * Needs page_size >= 64 and prefill-shaped units (tables whose sequences all
+ * bring more than 32 / G new rows, or any tables built for page_size < 64,
+ * are refused with SEGKV_ERR_UNSUPPORTED); split units are fine. Cached
+ * tokens (positions < c_b) get no mass.
+ */
+int segkv_attn_mass(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, const float *lse,
+                    float softmax_scale, float *mass, void *stream);
+
+/*
  * RoPE re-alignment of reused K pages (position-independent KV reuse; RedKnot
  * summary page, "Elastic Sparsity": recovery begins with RoPE position
  * alignment). entries: device int32 [n][4] = {page, slot0, nslots, delta}.

@@ -52,6 +52,12 @@ def load(path=_LIB):
                    P, P, P, P, P, P, P, P, ctypes.c_int64,
                    P, ctypes.c_int64, ctypes.c_double, P, P]
     fn.restype = ctypes.c_int
+    fm = lib.oracle_mass_fp64
+    fm.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                   P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   P, P, P, P, P, P, P, P, ctypes.c_int64,
+                   P, ctypes.c_int64, ctypes.c_double, P]
+    fm.restype = ctypes.c_int
     lib.oracle_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -151,3 +157,26 @@ def attention(k_pool, v_pool, q_bits, tables, queries, scale=None, lib_path=_LIB
     if rc != 0:
         raise ValueError(f"oracle_attn_fp64 failed with status {rc}")
     return o, lse
+
+
+def attention_mass(k_pool, q_bits, tables, queries, scale=None, lib_path=_LIB):
+    """fp64 attention mass of the new tokens (oracle_mass_fp64): float64 [sum n_b],
+    summed over the given (b, h, t) queries (normally all of them)."""
+    lib = load(lib_path)
+    num_pages, P, D = k_pool.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    queries = np.ascontiguousarray(queries, dtype=np.int32)
+    q_bits = np.ascontiguousarray(q_bits)
+    mass = np.zeros(q_bits.shape[0], dtype=np.float64)
+    arrs = {k: np.ascontiguousarray(tables[k], dtype=np.int32)
+            for k in ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "cu_pages", "page_list")}
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    rc = lib.oracle_mass_fp64(
+        ptr(k_pool), num_pages, P, D, ptr(q_bits), q_bits.shape[0], tables["hq"], tables["hkv"],
+        len(arrs["q_row0"]), ptr(arrs["q_row0"]), ptr(arrs["n_q"]), ptr(arrs["q_pos0"]), ptr(arrs["kv_head"]),
+        ptr(arrs["window"]), ptr(arrs["k_pos0"]), ptr(arrs["cu_pages"]), ptr(arrs["page_list"]),
+        len(arrs["page_list"]), ptr(queries), queries.shape[0], float(scale), ptr(mass))
+    if rc != 0:
+        raise ValueError(f"oracle_mass_fp64 failed with status {rc}")
+    return mass

@@ -1,0 +1,70 @@
+"""GPU parity of the attention mass of the new tokens (segkv_attn_mass)
+against the fp64 oracle (oracle_mass_fp64), through the C ABI.
+
+Bar: |mass - oracle| <= 4e-3 * oracle + 1e-5 per token. The kernel weighs
+each score with the attention kernel's own LSE, which is within 2e-3 of the
+exact one (the attention parity bar), so each weight is within about 2e-3
+relative; a sum of positive weights keeps that relative error. The float
+atomics make the summation order vary from run to run: results are checked
+against the oracle, not against each other bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import head_segmented_paged_amd as H
+from oracle import paged as opaged
+from oracle import tables as otables
+from tests.common import adhoc
+from tests.gpu_helpers import GpuLayer, host_bits, say
+from workloads import MISTRAL_8K, layer_tensors, realize
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def run_mass(w, max_unit_tiles=0):
+    r = realize(w)
+    say(f"[case] mass {w.name} hq {w.hq} hkv {w.hkv} D {w.d} P {w.page} "
+        f"seqs {list(zip(r.cached_len.tolist(), r.new_len.tolist()))[:4]} run {max_unit_tiles}")
+    t = layer_tensors(w, r, 0, device="cuda")
+    gl = GpuLayer(w, r, 0, t, max_unit_tiles=max_unit_tiles)
+    o, lse = gl.run()
+    mass = torch.empty(int(r.new_len.sum()), dtype=torch.float32, device="cuda")
+    H.segkv_attn_mass(gl.ctx, gl.dev, t["q"], lse, mass)
+    torch.cuda.synchronize()
+    bits = {k: host_bits(v) for k, v in t.items()}
+    tab = otables.build_tables(r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
+                               w.hq, w.hkv, w.page, r.num_pages)
+    kp, vp = opaged.empty_pools(r.num_pages, w.page, w.d)
+    opaged.scatter_pages(kp, vp, r.page_of[0], r.cached_len, r.new_len, bits["k_cached"], bits["v_cached"],
+                         bits["k_new"], bits["v_new"])
+    ref = opaged.attention_mass(kp, bits["q"], tab, opaged.all_queries(tab, w.hq))
+    got = mass.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    say(f"[ok] mass: max rel {np.max(err / np.maximum(ref, 1e-9)):.2e}, total {got.sum():.6g} vs {ref.sum():.6g}")
+    assert np.all(err <= 4e-3 * ref + 1e-5)
+    return got, ref
+
+
+MASS = [
+    # (hq, hkv, d, page, window, classes, seqs, longest run)
+    (8, 2, 128, 64, 100, (0, 1), ((0, 200), (37, 301), (1000, 77)), 0),
+    (16, 2, 64, 128, 300, (1, 0), ((250, 260), (0, 40)), 0),
+    (6, 3, 128, 256, 40, (1, 0, 0), ((700, 45), (3, 250)), 0),
+    (4, 4, 64, 64, 1, (1, 1, 0, 0), ((130, 70), (64, 64)), 2),
+    (8, 2, 128, 64, 2000, (1, 0), ((0, 513),), 3),
+]
+
+
+@pytest.mark.parametrize("case", MASS, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_w{c[4]}_run{c[7]}")
+def test_mass_all_tokens(case):
+    hq, hkv, d, page, window, classes, seqs, run = case
+    run_mass(adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * d + page),
+             max_unit_tiles=run)
+
+
+def test_mass_8k():
+    got, ref = run_mass(MISTRAL_8K)
+    # no cached prefix: every query's weights sum to one over the new tokens
+    assert abs(got.sum() - 32 * 8192) <= 1e-3 * 32 * 8192
