@@ -33,7 +33,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
-HIP_SOURCES = ["segkv_attn.hip", "segkv_pages.hip"]
+HIP_SOURCES = ["segkv_attn.hip", "segkv_pages.hip", "segkv_ffn.hip"]
 CXX_SOURCES = ["segkv_api.cpp", "segkv_tables.cpp"]
 
 

@@ -104,6 +104,20 @@ extern "C" int segkv_attn_mass(const segkv_ctx *ctx, const segkv_dev_tables *t, 
     return segkv::launch_attn_mass(cfg, *t, q, lse, scale * 1.44269504088896340736f, mass, stream);
 }
 
+extern "C" int segkv_select_tokens(const segkv_ctx *ctx, const float *mass, const int32_t *cu_rows,
+                                   const int32_t *keep, const int32_t *cu_keep, int32_t num_seqs,
+                                   int64_t total_rows, int32_t *rows_out, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "select_tokens: null context");
+    if (num_seqs < 0 || total_rows < 0 || total_rows > 0x7fffffff)
+        return fail(SEGKV_ERR_INVALID_ARG, "select_tokens: bad sizes");
+    if (num_seqs == 0) return SEGKV_OK;
+    if (!mass || !cu_rows || !keep || !cu_keep || !rows_out)
+        return fail(SEGKV_ERR_INVALID_ARG, "select_tokens: null pointer");
+    return segkv::launch_select_tokens(mass, cu_rows, keep, cu_keep, num_seqs, total_rows, rows_out, stream);
+}
+
 extern "C" int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, int64_t n, float rope_base,
                                   void *stream)
 {

@@ -88,6 +88,7 @@ def _load():
         "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
         "segkv_rope_realign": ([_P, _P, _i64, ctypes.c_float, _P], ctypes.c_int),
         "segkv_attn_mass": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+        "segkv_select_tokens": ([_P, _P, _P, _P, _P, _i32, _i64, _P, _P], ctypes.c_int),
         "segkv_last_error": ([], ctypes.c_char_p),
         "segkv_version": ([], ctypes.c_char_p),
     }
@@ -100,8 +101,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
-            "segkv_attn_prefill", "segkv_attn_mass", "segkv_gather_pages", "segkv_rope_realign", "segkv_last_error",
-            "segkv_version")
+            "segkv_attn_prefill", "segkv_attn_mass", "segkv_select_tokens", "segkv_gather_pages",
+            "segkv_rope_realign", "segkv_last_error", "segkv_version")
 
 
 def segkv_last_error() -> str:
@@ -272,6 +273,12 @@ def segkv_attn_mass(ctx, dev_tables, q, lse, mass, softmax_scale=0.0, stream=Non
     """Attention mass of the new tokens: mass fp32 [rows], lse fp32 [hq][rows] from segkv_attn_prefill."""
     _check(_lib.segkv_attn_mass(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(lse),
                                 float(softmax_scale), _ptr(mass), _stream(stream)))
+
+
+def segkv_select_tokens(ctx, mass, cu_rows, keep, cu_keep, rows_out, stream=None):
+    """Top-keep[b] rows of each sequence by mass (ties to the lower row), ascending, into rows_out."""
+    _check(_lib.segkv_select_tokens(ctx.handle, _ptr(mass), _ptr(cu_rows), _ptr(keep), _ptr(cu_keep),
+                                    keep.shape[0], mass.shape[0], _ptr(rows_out), _stream(stream)))
 
 
 def segkv_rope_realign(ctx, entries, rope_base=10000.0, stream=None):

@@ -300,6 +300,24 @@ int segkv_attn_mass(const segkv_ctx *ctx, const segkv_dev_tables *t, const void 
                     float softmax_scale, float *mass, void *stream);
 
 /*
+ * Sparse FFN token selection (RedKnot summary page, "Sparse FFN": the
+ * top-k tokens by attention score run the dense FFN, the rest the residual
+ * identity). For each sequence b, picks min(keep[b], n_b, cu_keep[b+1] -
+ * cu_keep[b]) of its rows cu_rows[b] .. cu_rows[b+1]-1 with the largest mass
+ * (ties to the lower row; zero, negative and NaN masses rank as zero) and
+ * writes their row indices in ascending order to rows_out[cu_keep[b] ...].
+ *   mass     : device fp32 [total_rows] (segkv_attn_mass)
+ *   cu_rows  : device int32 [num_seqs+1]; keep: device int32 [num_seqs];
+ *   cu_keep  : device int32 [num_seqs+1], the output offsets
+ *   rows_out : device int32 [cu_keep[num_seqs]]
+ * A sequence whose row range leaves [0, total_rows) is skipped. The result is
+ * unique (no order freedom), so it is reproducible bit for bit.
+ */
+int segkv_select_tokens(const segkv_ctx *ctx, const float *mass, const int32_t *cu_rows, const int32_t *keep,
+                        const int32_t *cu_keep, int32_t num_seqs, int64_t total_rows, int32_t *rows_out,
+                        void *stream);
+
+/*
  * RoPE re-alignment of reused K pages (position-independent KV reuse; RedKnot
  * summary page, "Elastic Sparsity": recovery begins with RoPE position
  * alignment). entries: device int32 [n][4] = {page, slot0, nslots, delta}.

@@ -68,3 +68,43 @@ def test_mass_8k():
     got, ref = run_mass(MISTRAL_8K)
     # no cached prefix: every query's weights sum to one over the new tokens
     assert abs(got.sum() - 32 * 8192) <= 1e-3 * 32 * 8192
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_tokens_matches_oracle(seed):
+    from oracle.sparse_ffn import select_tokens
+    rng = np.random.Generator(np.random.PCG64(100 + seed))
+    n = np.array([1, 7, 1023, 1024, 1025, 5000, 70000, 333])
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    mass = (np.round(rng.random(cu[-1]) * 50) / 7).astype(np.float32)       # ties, and exact zeros
+    mass[rng.random(cu[-1]) < 0.01] = np.nan
+    mass[rng.random(cu[-1]) < 0.01] = -1.0
+    keep = np.array([1, 0, 1000, 1024, 2000, 1, 17000, 333], dtype=np.int32)
+    k = np.minimum(keep, n)
+    cu_keep = np.concatenate([[0], np.cumsum(k)]).astype(np.int32)
+    say(f"[case] select seed {seed}: {len(n)} sequences, {cu[-1]} rows")
+    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 8, 2, 128, 64, num_pages=1)
+    dev = {name: torch.from_numpy(a).cuda() for name, a in
+           (("mass", mass), ("cu", cu), ("keep", keep), ("cu_keep", cu_keep))}
+    out = torch.full((int(cu_keep[-1]),), -7, dtype=torch.int32, device="cuda")
+    H.segkv_select_tokens(ctx, dev["mass"], dev["cu"], dev["keep"], dev["cu_keep"], out)
+    torch.cuda.synchronize()
+    expect = select_tokens(mass.astype(np.float64), cu, keep, cu_keep)
+    assert np.array_equal(out.cpu().numpy(), expect)
+
+
+def test_mass_then_select_8k():
+    """End to end on the 8K layer: mass from the attention's LSE, then the
+    top quarter of the tokens; the choice equals the oracle's on the same masses."""
+    from oracle.sparse_ffn import select_tokens
+    got, ref = run_mass(MISTRAL_8K)
+    n = got.shape[0]
+    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 32, 8, 128, 64, num_pages=1)
+    m = torch.from_numpy(got.astype(np.float32)).cuda()
+    cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    keep = torch.tensor([n // 4], dtype=torch.int32, device="cuda")
+    cu_keep = torch.tensor([0, n // 4], dtype=torch.int32, device="cuda")
+    out = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    H.segkv_select_tokens(ctx, m, cu, keep, cu_keep, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), select_tokens(got.astype(np.float32).astype(np.float64), [0, n], [n // 4]))
