@@ -239,6 +239,48 @@ def cpu_baseline(res, target_s=12.0):
     }
 
 
+def ffn_bench(torch, steps, warmup, tokens=8192, keep=2048, d_model=4096, d_ff=14336):
+    """The gathered SwiGLU FFN of `keep` chosen tokens out of `tokens` (a
+    Mistral-7B-sized block, random weights), timed with HIP events; the same
+    kernels over every token give the dense FFN time for comparison."""
+    import head_segmented_paged_amd as H
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn((tokens, d_model), device="cuda", dtype=torch.bfloat16, generator=g)
+    w = [(torch.randn(shape, device="cuda", dtype=torch.float32, generator=g) / shape[1] ** 0.5).to(torch.bfloat16)
+         for shape in ((d_ff, d_model), (d_ff, d_model), (d_model, d_ff))]
+    ctx = H.segkv_create(x, x, 32, 8, 128, 64, num_pages=1)
+    rng = np.random.Generator(np.random.PCG64(5))
+    sel = torch.from_numpy(np.sort(rng.choice(tokens, keep, replace=False)).astype(np.int32)).cuda()
+    dense = torch.arange(tokens, dtype=torch.int32, device="cuda")
+    h = torch.empty((tokens, d_ff), dtype=torch.bfloat16, device="cuda")
+
+    def timeit(rows):
+        for _ in range(warmup):
+            H.segkv_sparse_ffn(ctx, x, rows, *w, h=h)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            H.segkv_sparse_ffn(ctx, x, rows, *w, h=h)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    ms = timeit(sel)
+    ms_dense = timeit(dense)
+    flops = 3 * 2.0 * keep * d_model * d_ff
+    tf = flops / (ms / 1e3) / 1e12
+    return {"metric": "sparse FFN of the chosen tokens (gathered SwiGLU, bf16 MFMA)", "value": tf,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"sparse_ffn_{keep}of{tokens}_dm{d_model}_dff{d_ff}", "tokens": tokens,
+                       "chosen": keep, "d_model": d_model, "d_ff": d_ff},
+            "dense_ms_all_tokens": ms_dense,
+            "dense_tflops_all_tokens": 3 * 2.0 * tokens * d_model * d_ff / (ms_dense / 1e3) / 1e12,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16_TFLOPS, "traffic": None}}
+
+
 def rope_bench(torch, n_pages, steps, warmup, P=64, D=128):
     """RoPE re-alignment of n_pages whole K pages (each turned by its own
     delta), timed with HIP events on the launch stream. Bytes = every K page
@@ -298,6 +340,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
+    ap.add_argument("--sparse-ffn", action="store_true",
+                    help="only time the sparse FFN of 2048 chosen of 8192 tokens (d_model 4096, d_ff 14336)")
     ap.add_argument("--rope-pages", type=int, default=0, metavar="N",
                     help="only time the RoPE re-alignment of N reused K pages (P 64, D 128), in GB/s")
     args = ap.parse_args()
@@ -318,6 +362,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.sparse_ffn:
+        print(json.dumps(ffn_bench(torch, args.steps, args.warmup)), flush=True)
         return
     if args.rope_pages:
         print(json.dumps(rope_bench(torch, args.rope_pages, args.steps, args.warmup)), flush=True)

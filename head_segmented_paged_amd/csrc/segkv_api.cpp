@@ -118,6 +118,30 @@ extern "C" int segkv_select_tokens(const segkv_ctx *ctx, const float *mass, cons
     return segkv::launch_select_tokens(mass, cu_rows, keep, cu_keep, num_seqs, total_rows, rows_out, stream);
 }
 
+extern "C" int segkv_sparse_ffn(const segkv_ctx *ctx, void *x, int64_t x_rows, int32_t d_model, int32_t d_ff,
+                                const int32_t *sel_rows, int64_t n_sel, const void *w_gate, const void *w_up,
+                                const void *w_down, void *h, int64_t h_bytes, void *stream)
+{
+    segkv::clear_error();
+    if (!ctx) return fail(SEGKV_ERR_INVALID_ARG, "sparse_ffn: null context");
+    if (x_rows < 0 || n_sel < 0 || n_sel > 0x7fffffff || d_model < 1 || d_ff < 1)
+        return fail(SEGKV_ERR_INVALID_ARG, "sparse_ffn: bad sizes");
+    if (d_model % 128 != 0 || d_ff % 128 != 0)
+        return fail(SEGKV_ERR_UNSUPPORTED, "sparse_ffn: d_model (%d) and d_ff (%d) must be multiples of 128",
+                    d_model, d_ff);
+    if (x_rows * d_model * 2 > 0xffffffffll || static_cast<int64_t>(d_ff) * d_model * 2 > 0xffffffffll ||
+        n_sel * d_ff * 2 > 0xffffffffll)
+        return fail(SEGKV_ERR_UNSUPPORTED, "sparse_ffn: an operand exceeds 4 GiB");
+    if (n_sel == 0) return SEGKV_OK;
+    if (!x || !sel_rows || !w_gate || !w_up || !w_down || !h)
+        return fail(SEGKV_ERR_INVALID_ARG, "sparse_ffn: null pointer");
+    if (h_bytes < n_sel * d_ff * 2)
+        return fail(SEGKV_ERR_CAPACITY, "sparse_ffn: workspace h needs %lld bytes, %lld given",
+                    static_cast<long long>(n_sel * d_ff * 2), static_cast<long long>(h_bytes));
+    return segkv::launch_sparse_ffn(x, x_rows, d_model, d_ff, sel_rows, static_cast<int32_t>(n_sel), w_gate, w_up,
+                                    w_down, h, stream);
+}
+
 extern "C" int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, int64_t n, float rope_base,
                                   void *stream)
 {

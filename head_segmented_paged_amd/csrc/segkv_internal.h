@@ -66,6 +66,8 @@ int launch_gather_pages(const segkv_config &cfg, const int32_t *page_ids, int64_
 int launch_rope_realign(const segkv_config &cfg, const int32_t *entries, int64_t n, float rope_base, void *stream);
 int launch_select_tokens(const float *mass, const int32_t *cu_rows, const int32_t *keep, const int32_t *cu_keep,
                          int32_t num_seqs, int64_t total_rows, int32_t *rows_out, void *stream);
+int launch_sparse_ffn(void *x, int64_t x_rows, int32_t d_model, int32_t d_ff, const int32_t *sel_rows,
+                      int32_t n_sel, const void *w_gate, const void *w_up, const void *w_down, void *h, void *stream);
 int launch_attn_mass(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, const float *lse,
                      float scale_log2, float *mass, void *stream);
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,

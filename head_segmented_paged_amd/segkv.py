@@ -89,6 +89,7 @@ def _load():
         "segkv_rope_realign": ([_P, _P, _i64, ctypes.c_float, _P], ctypes.c_int),
         "segkv_attn_mass": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
         "segkv_select_tokens": ([_P, _P, _P, _P, _P, _i32, _i64, _P, _P], ctypes.c_int),
+        "segkv_sparse_ffn": ([_P, _P, _i64, _i32, _i32, _P, _i64, _P, _P, _P, _P, _i64, _P], ctypes.c_int),
         "segkv_last_error": ([], ctypes.c_char_p),
         "segkv_version": ([], ctypes.c_char_p),
     }
@@ -101,7 +102,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
-            "segkv_attn_prefill", "segkv_attn_mass", "segkv_select_tokens", "segkv_gather_pages",
+            "segkv_attn_prefill", "segkv_attn_mass", "segkv_select_tokens", "segkv_sparse_ffn", "segkv_gather_pages",
             "segkv_rope_realign", "segkv_last_error", "segkv_version")
 
 
@@ -279,6 +280,18 @@ def segkv_select_tokens(ctx, mass, cu_rows, keep, cu_keep, rows_out, stream=None
     """Top-keep[b] rows of each sequence by mass (ties to the lower row), ascending, into rows_out."""
     _check(_lib.segkv_select_tokens(ctx.handle, _ptr(mass), _ptr(cu_rows), _ptr(keep), _ptr(cu_keep),
                                     keep.shape[0], mass.shape[0], _ptr(rows_out), _stream(stream)))
+
+
+def segkv_sparse_ffn(ctx, x, sel_rows, w_gate, w_up, w_down, h=None, stream=None):
+    """x bf16 [rows][d_model] updated in place for the rows in sel_rows (int32 device);
+    weights bf16 [d_ff][d_model] (gate, up) and [d_model][d_ff] (down); h: bf16 workspace or None."""
+    import torch
+    n_sel, d_ff, d_model = sel_rows.shape[0], w_gate.shape[0], x.shape[1]
+    if h is None:
+        h = torch.empty((max(n_sel, 1), d_ff), dtype=torch.bfloat16, device=x.device)
+    _check(_lib.segkv_sparse_ffn(ctx.handle, _ptr(x), x.shape[0], d_model, d_ff, _ptr(sel_rows), n_sel,
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), h.numel() * h.element_size(),
+                                 _stream(stream)))
 
 
 def segkv_rope_realign(ctx, entries, rope_base=10000.0, stream=None):

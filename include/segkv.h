@@ -318,6 +318,25 @@ int segkv_select_tokens(const segkv_ctx *ctx, const float *mass, const int32_t *
                         void *stream);
 
 /*
+ * Sparse FFN of the chosen tokens (RedKnot summary page, "Sparse FFN"),
+ * a SwiGLU block applied in place as a residual:
+ *   h[m]          = bf16( silu(Wg x[r_m]) * (Wu x[r_m]) )   silu(g) = g / (1 + e^-g)
+ *   x[r_m]        = bf16( x[r_m] + Wd h[m] )
+ * for the chosen rows r_m = sel_rows[m], m < n_sel (distinct; rows outside
+ * [0, x_rows) are skipped); every other row of x keeps its value (the
+ * residual identity path).
+ *   x      : device bf16 [x_rows][d_model], updated in place
+ *   w_gate, w_up : device bf16 [d_ff][d_model];  w_down : device bf16 [d_model][d_ff]
+ *   h      : device workspace, at least n_sel * d_ff * 2 bytes (bf16 [n_sel][d_ff])
+ * Products accumulate in fp32 on bf16 MFMA. d_model and d_ff must be
+ * multiples of 128 (SEGKV_ERR_UNSUPPORTED otherwise) and every operand under
+ * 4 GiB.
+ */
+int segkv_sparse_ffn(const segkv_ctx *ctx, void *x, int64_t x_rows, int32_t d_model, int32_t d_ff,
+                     const int32_t *sel_rows, int64_t n_sel, const void *w_gate, const void *w_up,
+                     const void *w_down, void *h, int64_t h_bytes, void *stream);
+
+/*
  * RoPE re-alignment of reused K pages (position-independent KV reuse; RedKnot
  * summary page, "Elastic Sparsity": recovery begins with RoPE position
  * alignment). entries: device int32 [n][4] = {page, slot0, nslots, delta}.

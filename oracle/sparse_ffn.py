@@ -33,3 +33,41 @@ def select_tokens(mass, cu_rows, keep, cu_keep=None):
         order = np.lexsort((rows, -score))             # larger score first, then lower row
         out[cu_keep[b]:cu_keep[b] + k] = np.sort(rows[order[:k]])
     return out
+
+
+def _bits_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _to_bf16_bits(x):
+    """fp64 -> bf16 bits, rounded once to 8 significant bits, ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(m * 256.0), e - 8)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_hidden(x_bits, rows, wg_bits, wu_bits):
+    """h = bf16(silu(Wg x) * (Wu x)) for the chosen rows, in fp64 before the one rounding."""
+    x = _bits_to_f64(np.asarray(x_bits)[np.asarray(rows)])
+    g = x @ _bits_to_f64(wg_bits).T
+    u = x @ _bits_to_f64(wu_bits).T
+    return _to_bf16_bits(silu(g) * u)
+
+
+def residual_down(x_bits, rows, h_bits, wd_bits):
+    """The new bf16 rows x + Wd h (fp64, one rounding)."""
+    x = _bits_to_f64(np.asarray(x_bits)[np.asarray(rows)])
+    return _to_bf16_bits(x + _bits_to_f64(h_bits) @ _bits_to_f64(wd_bits).T)
+
+
+def sparse_ffn(x_bits, rows, wg_bits, wu_bits, wd_bits):
+    """Whole step on a host copy: returns (new x bits, h bits)."""
+    h = swiglu_hidden(x_bits, rows, wg_bits, wu_bits)
+    out = np.array(x_bits, copy=True)
+    out[np.asarray(rows)] = residual_down(x_bits, rows, h, wd_bits)
+    return out, h

@@ -108,3 +108,55 @@ def test_mass_then_select_8k():
     H.segkv_select_tokens(ctx, m, cu, keep, cu_keep, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), select_tokens(got.astype(np.float32).astype(np.float64), [0, n], [n // 4]))
+
+
+@pytest.mark.parametrize("dm,dff,rows,nsel", [(256, 512, 300, 77), (128, 384, 50, 50), (4096, 14336, 1024, 200)])
+def test_sparse_ffn_matches_oracle(dm, dff, rows, nsel):
+    """h against the oracle's bf16 hidden; x's chosen rows against the oracle's
+    residual computed from the kernel's own h (so one rounding of difference
+    is checked at a time); every other row bit for bit unchanged.
+    Bar: |got - ref| <= one bf16 ulp of ref + 2^-20 x (the sum of the absolute
+    terms that formed the value), and at most 1 % of the values off at all.
+    fp32 sums over d_model or d_ff terms are within ~1e-6 of the sum of
+    absolute terms; where those terms cancel, that is the bound that holds,
+    and otherwise only values that close to a rounding midpoint can round the
+    other way."""
+    from oracle import sparse_ffn as osf
+    say(f"[case] sparse ffn d_model {dm} d_ff {dff} rows {rows} chosen {nsel}")
+    g = torch.Generator(device="cpu").manual_seed(dm + nsel)
+    x = torch.randn((rows, dm), generator=g).to(torch.bfloat16)
+    wg = (torch.randn((dff, dm), generator=g) / dm ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn((dff, dm), generator=g) / dm ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn((dm, dff), generator=g) / dff ** 0.5).to(torch.bfloat16)
+    sel = np.sort(np.random.Generator(np.random.PCG64(nsel)).choice(rows, nsel, replace=False)).astype(np.int32)
+    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 8, 2, 128, 64, num_pages=1)
+    xd = x.cuda()
+    h = torch.empty((nsel, dff), dtype=torch.bfloat16, device="cuda")
+    H.segkv_sparse_ffn(ctx, xd, torch.from_numpy(sel).cuda(), wg.cuda(), wu.cuda(), wd.cuda(), h)
+    torch.cuda.synchronize()
+    b = lambda t: t.view(torch.int16).numpy().view(np.uint16)    # noqa: E731
+    xb, hb = b(xd.cpu()), b(h.cpu())
+    x0 = b(x)
+    h_ref = osf.swiglu_hidden(x0, sel, b(wg), b(wu))
+    y_ref = osf.residual_down(x0, sel, hb, b(wd))
+
+    def ulp_check(got, ref, absterms, what):
+        gf = osf._bits_to_f64(got)
+        rf = osf._bits_to_f64(ref)
+        spacing = np.ldexp(1.0, np.frexp(np.maximum(np.abs(rf), 1e-30))[1] - 8)   # bf16 ulp at |ref|
+        off = np.abs(gf - rf) > 0
+        say(f"[ok] {what}: {off.mean():.2e} of values off")
+        assert np.all(np.abs(gf - rf) <= spacing * 1.0001 + 2.0 ** -20 * absterms)
+        assert off.mean() <= 0.01
+
+    f = osf._bits_to_f64
+    xs = f(x0[sel])
+    g_, u_ = xs @ f(b(wg)).T, xs @ f(b(wu)).T
+    ag, au = np.abs(xs) @ np.abs(f(b(wg))).T, np.abs(xs) @ np.abs(f(b(wu))).T
+    h_terms = 1.1 * ag * np.abs(u_) + np.abs(osf.silu(g_)) * au
+    y_terms = np.abs(xs) + np.abs(f(hb)) @ np.abs(f(b(wd))).T
+    ulp_check(hb, h_ref, h_terms, "h")
+    ulp_check(xb[sel], y_ref, y_terms, "x chosen rows")
+    keep = np.ones(rows, bool)
+    keep[sel] = False
+    assert np.array_equal(xb[keep], x0[keep])

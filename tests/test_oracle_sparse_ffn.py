@@ -49,3 +49,39 @@ def test_selection_small_by_hand():
     assert select_tokens(mass, [0, 7], [7]).tolist() == list(range(7))  # NaN and -1 rank as zero, last
     assert select_tokens(mass, [0, 3, 7], [1, 2]).tolist() == [1, 3, 6]  # second sequence: 1.0 and the first 0.5
     assert select_tokens(mass, [0, 3, 7], [5, 0], cu_keep=[0, 2, 2]).tolist() == [0, 1]   # room clamps
+
+
+def _bits(x):
+    from oracle.sparse_ffn import _to_bf16_bits
+    return _to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def test_ffn_by_hand():
+    """d_model 2, d_ff 2, one chosen row: the SwiGLU block written out."""
+    import math
+    from oracle.sparse_ffn import sparse_ffn, _bits_to_f64
+    x = np.array([[1.0, 0.5], [2.0, -1.0]])
+    wg = np.array([[1.0, 0.0], [0.5, 1.0]])
+    wu = np.array([[2.0, 1.0], [0.0, -1.0]])
+    wd = np.array([[1.0, 0.25], [-0.5, 1.0]])
+    out, h = sparse_ffn(_bits(x), [1], _bits(wg), _bits(wu), _bits(wd))
+    g = [2.0, 0.0]                                     # Wg x1 = (2, 1 - 1)
+    u = [3.0, 1.0]                                     # Wu x1 = (4 - 1, 1)
+    hv = [g[0] / (1 + math.exp(-g[0])) * u[0], 0.0]
+    assert np.array_equal(h[0], _bits(hv))
+    hb = _bits_to_f64(_bits(hv))
+    y = [2.0 + 1.0 * hb[0] + 0.25 * hb[1], -1.0 - 0.5 * hb[0] + 1.0 * hb[1]]
+    assert np.array_equal(out[1], _bits(y))
+    assert np.array_equal(out[0], _bits(x[0]))        # not chosen: the residual identity
+
+
+def test_ffn_closed_forms():
+    from oracle.sparse_ffn import sparse_ffn, silu, _bits_to_f64
+    rng = np.random.Generator(np.random.PCG64(3))
+    x = _bits(rng.standard_normal((9, 8)))
+    wg, wd = _bits(rng.standard_normal((16, 8))), _bits(rng.standard_normal((8, 16)))
+    out, h = sparse_ffn(x, [2, 5], wg, _bits(np.zeros((16, 8))), wd)    # zero up projection: no change
+    assert np.array_equal(out, x) and not _bits_to_f64(h).any()        # (signed zeros)
+    g = np.linspace(-6, 6, 25)
+    np.testing.assert_allclose(silu(g) - silu(-g), g, atol=1e-12)      # silu(g) - silu(-g) = g
+    assert silu(0.0) == 0.0
