@@ -77,6 +77,10 @@ struct Staged {
 // K row fed to MFMA row r: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int swizzle_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// NaN-propagating maximum (v_maximum3_f32 in chains): unlike fmaxf it needs no
+// quieting of its operands.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Lanes l and l ^ 32 exchange x through v_permlane32_swap (upper half of the
 // first operand <-> lower half of the second). The second operand is a copy
 // the compiler cannot see through: with two operands it can prove equal it
@@ -94,7 +98,7 @@ __device__ __forceinline__ float max_halves(float x)
 {
     float a, b;
     swap_halves(x, a, b);
-    return fmaxf(a, b);
+    return vmax(a, b);
 }
 
 __device__ __forceinline__ float sum_halves(float x)
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+                for (int e = 0; e < 16; ++e) mt = vmax(mt, sacc[kb][e]);
             mt = max_halves(mt) * scale_log2;
             if (__any(mt > m + kRescaleSlack)) {
                 const float m_new = fmaxf(m, mt);
@@ -728,16 +732,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
                     sc[h][e] = static_cast<unsigned>(off + kc) <= span ? sc[h][e] : -__builtin_inff();
                 }
         }
-        // Tile max: four independent chains of three-operand maxima.
+        // Tile max: four independent chains of three-operand maxima. The
+        // NaN-propagating maximum needs no quieting of the MFMA results
+        // (v_maximum3_f32); a NaN score would reach O through P either way.
         float mx[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e0 = 8 * (c & 1);
-            mx[c] = fmaxf(sc[c >> 1][e0], sc[c >> 1][e0 + 1]);
+            mx[c] = vmax(sc[c >> 1][e0], sc[c >> 1][e0 + 1]);
 #pragma unroll
-            for (int e = 2; e < 8; e += 2) mx[c] = fmaxf(fmaxf(mx[c], sc[c >> 1][e0 + e]), sc[c >> 1][e0 + e + 1]);
+            for (int e = 2; e < 8; e += 2) mx[c] = vmax(vmax(mx[c], sc[c >> 1][e0 + e]), sc[c >> 1][e0 + e + 1]);
         }
-        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        float mt = vmax(vmax(mx[0], mx[1]), vmax(mx[2], mx[3]));
         mt = max_halves(mt) * scale_log2;
         if (__any(mt > m + kRescaleSlack)) {
             const float m_new = fmaxf(m, mt);
@@ -1056,9 +1062,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
                 sacc[e] = (pos >= lo_eff && pos <= hi_eff) ? sacc[e] : -__builtin_inff();
             }
         }
-        float mx = fmaxf(sacc[0], sacc[1]);
+        float mx = vmax(sacc[0], sacc[1]);
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, sacc[e]), sacc[e + 1]);
+        for (int e = 2; e < 16; e += 2) mx = vmax(vmax(mx, sacc[e]), sacc[e + 1]);
         const float mt = max_halves(mx) * scale_log2;
         if (__any(mt > m + kRescaleSlack)) {
             const float m_new = fmaxf(m, mt);
