@@ -891,26 +891,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
 // Decode / small-chunk kernel (pages of at least one tile). A unit is one
 // segment's few new rows for all G query heads of its KV head: column c of
 // the MFMAs is the (row c / G, head c % G) pair, so the 32 columns carry up to
-// 32 / G rows. The unit's run of 64-key tiles is read two tiles (128 keys) at
-// a time into a two-stage LDS ring, and each wavefront takes its own 32 keys
-// of the pair: wave w reads keys 32 (w & 1) .. +31 of tile (w >> 1). Each wave
-// keeps its own running maximum, sum and O^T; at the end the four combine
-// through LDS as blocks of one online softmax. The step is bound by HBM
-// bandwidth, and the 128 KB ring keeps 64 KB of K/V in flight per CU.
+// 32 / G rows. The step is bound by HBM bandwidth, so the kernel is built to
+// keep bytes in flight: every wavefront streams its own 32-key blocks of the
+// unit's run (blocks w, w + 4, ...) straight into its MFMA operand registers,
+// loading the next block while it computes the current one, with no LDS and
+// no barrier in the loop; two workgroups per CU. Each wave keeps its own
+// running maximum, sum and O^T; at the end the four combine through LDS as
+// blocks of one online softmax.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
     int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
     int32_t hq, int32_t unit_rows, int32_t unit_heads, float scale_log2, void *__restrict__ o,
     float *__restrict__ lse, float *__restrict__ parts, int32_t num_parts)
 {
-    using T = DmaTile<D>;
     constexpr int kSteps = D / 16;
     constexpr int kDBlocks = D / 32;
     constexpr int kLd = D + 4;   // floats per (wave, column) row of the combine buffer
-    __shared__ __attribute__((aligned(1024))) char stage0[2 * T::bytes];
-    __shared__ __attribute__((aligned(1024))) char stage1[2 * T::bytes];
+    constexpr int kBlock = 32;   // keys per block
+    __shared__ __attribute__((aligned(16))) float cbuf[kWaves * kWaveRows * kLd];
 
     const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
@@ -925,141 +925,145 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
     const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
     const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
     const int page_off = desc[SEGKV_SEG_PAGE_OFF];
-    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
+    // k_pos0 starts a page, so a 32-key block never crosses one.
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1 ||
+        (k_pos0 & ((1 << log2P) - 1)) != 0)
+        return;
     int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
     if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
     const int32_t *pages = page_list + page_off;
+    const int P = 1 << log2P;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
-    const int sub = wave >> 1, kh = wave & 1;   // this wave's tile of the pair and 32-key half
 
-    // Rows of the unit and its band of tiles, cut to the unit's run.
+    // Rows of the unit and its band of tiles, cut to the unit's run; in 32-key blocks.
     const int unit_end = min(row0 + unit_rows, n_q);
     const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
     const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
     const int tile_beg = max((lo_pos - k_pos0) / kBK, run0);
     const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
-    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
+    const int blk_beg = 2 * tile_beg, blk_end = 2 * tile_end;
+    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);   // stored and visible keys
     const int zero_hi = k_len;
 
     // This lane's column: (row, head) pair, its query position and the keys it
     // may see inside the run.
-    const int pr = col / unit_heads, ph = col % unit_heads;
-    const bool col_ok = col < unit_rows * unit_heads && row0 + pr < n_q && head0 + ph < hq;
-    const int my_t = min(row0 + pr, n_q - 1);
-    const int head = min(head0 + ph, hq - 1);
+    const int my_t = min(row0 + col / unit_heads, n_q - 1);
     const int my_pos = q_pos0 + my_t;
-    const int64_t my_row = static_cast<int64_t>(q_row0) + my_t;
     const int run_lo = k_pos0 + tile_beg * kBK, run_hi = k_pos0 + tile_end * kBK - 1;
     const int lo_eff = max(window ? my_pos - window + 1 : 0, run_lo);
     const int hi_eff = min(my_pos, run_hi);
-    // Keys every column may see (tiles inside need no mask).
     const int all_lo = max(window ? last_pos - window + 1 : 0, run_lo);
     const int all_hi = min(first_pos, run_hi);
 
-    bf16x8 qreg[kSteps];
-    {
-        const bool can_load = col_ok && my_row < total_q_rows;
-        const u16 *qp = q + (my_row * hq + head) * D + 8 * half;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
-            qreg[s] = __builtin_bit_cast(bf16x8, raw);
+    // Q^T (the B operand, lane column = pair) sits in LDS for the loop, in the
+    // combine buffer's space, rows padded by 16 bytes so the lanes' 16-byte
+    // reads fall in distinct banks.
+    constexpr int kQLd = D + 8;   // bf16 per column row
+    static_assert(kWaveRows * kQLd * 2 <= static_cast<int>(sizeof(cbuf)), "Q^T must fit the combine buffer");
+    u16 *qlds = reinterpret_cast<u16 *>(cbuf);
+    for (int i = threadIdx.x; i < kWaveRows * (D / 8); i += kThreads) {
+        const int qc = i / (D / 8), qd = 8 * (i % (D / 8));
+        const int qr = qc / unit_heads, qh = qc % unit_heads;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (qc < unit_rows * unit_heads && row0 + qr < n_q && head0 + qh < hq) {
+            const int64_t qrow = static_cast<int64_t>(q_row0) + row0 + qr;
+            if (qrow < total_q_rows) raw = *reinterpret_cast<const u32x4 *>(q + (qrow * hq + head0 + qh) * D + qd);
         }
+        *reinterpret_cast<u32x4 *>(qlds + qc * kQLd + qd) = raw;
     }
+    const u16 *qcol = qlds + col * kQLd + 8 * half;
     f32x16 oacc[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
     float m = kNegBig, lsum = 0.f;
 
-    int win = ((tile_beg * kBK) >> log2P) >> 6;
-    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
-    int win_cur = load_window(win), win_next = load_window(win + 1);
-    auto tile_page = [&](int jt) {
-        const int lp = (jt * kBK) >> log2P;
-        if ((lp >> 6) != win) {
-            win = lp >> 6;
-            win_cur = win_next;
-            win_next = load_window(win + 1);
-        }
-        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
-        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    // Page ids of the run, staged in LDS after Q^T a pass of kIdCap pages at a
+    // time (k_pos0 starts a page, so entry e holds keys e P .. e P + P - 1).
+    constexpr int kIdCap = 4096;
+    static_assert(kWaveRows * kQLd * 2 + kIdCap * 4 <= static_cast<int>(sizeof(cbuf)), "page ids must fit");
+    int32_t *ids = reinterpret_cast<int32_t *>(cbuf + kWaveRows * kQLd / 2);
+    const int blocks_per_page = P / kBlock;
+    const int blocks_per_pass = kIdCap * blocks_per_page;
+
+    // Operands of one 32-key block, read from its page with buffer loads (a
+    // missing page or a block past the pass has an empty range: zeros, no
+    // traffic, and every path issues the same loads, so the waits the compiler
+    // places before using a block count only that block's loads). K: the A
+    // operand of S^T = K . Q^T, lane row swizzle_row(col) (so S^T registers are
+    // the P^T operand), 8 dims at 16 s + 8 half. V^T: the A operand of
+    // O^T += V^T . P^T, row d = 32 db + col, keys 16 t + 8 half .. + 7.
+    struct Ops {
+        bf16x8 k[kSteps];
+        bf16x8 v[2][kDBlocks];
+    };
+    const unsigned k_lane = static_cast<unsigned>((swizzle_row(col) * D + 8 * half) * 2);
+    const unsigned v_lane = static_cast<unsigned>((col * P + 8 * half) * 2);
+    int pass_beg = blk_beg, pass_end = blk_beg, id0 = 0;
+    auto page_of = [&](int blk) -> int {
+        int page = -1;
+        if (blk < pass_end) page = __builtin_amdgcn_readfirstlane(ids[blk / blocks_per_page - id0]);
+        return page;
+    };
+    auto fetch_k = [&](Ops &op, int blk) {
+        const int page = page_of(blk);
+        const int pg = max(page, 0);
+        const __amdgpu_buffer_rsrc_t rk =
+            page_rsrc(kpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
+        const unsigned off = k_lane + static_cast<unsigned>(((blk * kBlock) & (P - 1)) * D * 2);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            op.k[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 32 * s, 0, 0));
+    };
+    auto fetch_v = [&](Ops &op, int blk) {
+        const int page = page_of(blk);
+        const int pg = max(page, 0);
+        const __amdgpu_buffer_rsrc_t rv =
+            page_rsrc(vpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
+        const unsigned off = v_lane + static_cast<unsigned>(((blk * kBlock) & (P - 1)) * 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db)
+                op.v[t][db] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off + 64 * db * P + 32 * t, 0, 0));
     };
 
-    unsigned kdma[T::kInstr], vdma[T::vInstr];
+    // One block; the next block's V is requested once this block's K is used.
+    auto compute = [&](Ops &op, int blk, Ops &nxt, int nxt_blk) {
+        const int key0 = blk * kBlock;
+        // V entries outside the stored-and-visible range may hold anything
+        // (0 * NaN would reach O): clear them on the blocks that have any.
+        if (key0 < zero_lo || key0 + kBlock > zero_hi) {
 #pragma unroll
-    for (int i = 0; i < T::kInstr; ++i) {
-        const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
-        const int r = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(r);
-        kdma[i] = static_cast<unsigned>(r * T::kRowBytes + c * 16);
-    }
+            for (int t = 0; t < 2; ++t) {
+                u32x4 keep;
 #pragma unroll
-    for (int i = 0; i < T::vInstr; ++i) {
-        const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
-        const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
-        vdma[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
-    }
-    // Tiles jt and jt + 1 into one stage (a tile past the run reads zeros).
-    auto dma_pair = [&](char *stage, int jt) {
+                for (int w = 0; w < 4; ++w) {
+                    const int idx = key0 + 16 * t + 8 * half + 2 * w;
+                    keep[w] = ((idx >= zero_lo && idx < zero_hi) ? 0xffffu : 0u) |
+                              ((idx + 1 >= zero_lo && idx + 1 < zero_hi) ? 0xffff0000u : 0u);
+                }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tj = jt + i;
-            const int page = tj < tile_end ? tile_page(tj) : -1;
-            const unsigned slot0 = static_cast<unsigned>((tj * kBK) & ((1 << log2P) - 1));
-            const int64_t pg = page >= 0 ? page : 0;
-            const __amdgpu_buffer_rsrc_t rk =
-                page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
-            const __amdgpu_buffer_rsrc_t rv =
-                page_rsrc(vpool + ((pg * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
-            char *dst = stage + i * T::bytes;
-#pragma unroll
-            for (int k = 0; k < T::kInstr; ++k)
-                dma16(rk, dst + (wave * T::kInstr + k) * 1024, kdma[k], slot0 * T::kRowBytes);
-#pragma unroll
-            for (int k = 0; k < T::vInstr; ++k)
-                dma16(rv, dst + T::kBytes + (wave * T::vInstr + k) * 1024, vdma[k], slot0 * 2);
+                for (int db = 0; db < kDBlocks; ++db)
+                    op.v[t][db] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, op.v[t][db]) & keep);
+            }
         }
-    };
-    auto edge_pair = [&](int jt) {
-        const int key0 = jt * kBK;
-        return key0 < zero_lo || key0 + 2 * kBK > zero_hi;
-    };
-    auto fixup_pair = [&](char *stage, int jt) {
-        for (int e = threadIdx.x; e < 2 * D * kBK; e += kThreads) {
-            const int i = e / (D * kBK), d = (e / kBK) % D, k = e % kBK, idx = (jt + i) * kBK + k;
-            if (idx < zero_lo || idx >= zero_hi)
-                *reinterpret_cast<u16 *>(stage + i * T::bytes + T::kBytes + d * 128 + (((k >> 3) ^ vswz(d)) << 4) +
-                                         (k & 7) * 2) = 0;
-        }
-    };
-
-    const int krow = kh * 32 + swizzle_row(col);
-    unsigned ka[kSteps], va[2];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-        ka[s] = static_cast<unsigned>(sub * T::bytes + krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        va[t] = static_cast<unsigned>(sub * T::bytes + T::kBytes + col * 128 +
-                                      (((2 * (2 * kh + t) + half) ^ vswz(col)) << 4));
-
-    auto compute = [&](const char *stage, int jt) {
         f32x16 sacc = {};
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + ka[s]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc, 0, 0, 0);
-        }
-        // Keys of this wave: k_pos0 + (jt + sub) * 64 + 32 kh + 16 t + 8 half + i.
-        const int kp0 = k_pos0 + (jt + sub) * kBK + kh * 32;
-        if (!(kp0 >= all_lo && kp0 + 31 <= all_hi)) {
+        for (int s = 0; s < kSteps; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                op.k[s], *reinterpret_cast<const bf16x8 *>(qcol + 16 * s), sacc, 0, 0, 0);
+        fetch_v(nxt, nxt_blk);
+        const int kp0 = k_pos0 + key0;
+        const bool live = blk < pass_end;   // a block past the pass belongs to the next one
+        if (!(live && kp0 >= all_lo && kp0 + kBlock - 1 <= all_hi)) {
             const int kbase = kp0 + 8 * half;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int pos = kbase + 16 * (e >> 3) + (e & 7);
-                sacc[e] = (pos >= lo_eff && pos <= hi_eff) ? sacc[e] : -__builtin_inff();
+                sacc[e] = (live && pos >= lo_eff && pos <= hi_eff) ? sacc[e] : -__builtin_inff();
             }
         }
         float mx = vmax(sacc[0], sacc[1]);
@@ -1082,75 +1086,74 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
                 pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * t + i], scale_log2, -m)));
             lsum = sum8_bf16(pb, lsum);
 #pragma unroll
-            for (int db = 0; db < kDBlocks; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(stage + va[t] + db * 32 * 128);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-            }
+            for (int db = 0; db < kDBlocks; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v[t][db], pb, oacc[db], 0, 0, 0);
         }
     };
 
-    if (tile_beg < tile_end) {
-        dma_pair(stage0, tile_beg);
-        __syncthreads();
-        if (edge_pair(tile_beg)) {
-            fixup_pair(stage0, tile_beg);
-            __syncthreads();
+    // Passes over the pages of each kIdCap-page stretch of the segment; in
+    // each, wave w takes blocks w, w + 4, ... two at a time (a block past the
+    // pass is all masked and reads nothing), the next block loading while one
+    // computes.
+    for (; pass_beg < blk_end; pass_beg = pass_end) {
+        pass_end = min(blk_end, (pass_beg / blocks_per_pass + 1) * blocks_per_pass);
+        id0 = pass_beg / blocks_per_page;
+        const int n_ids = (pass_end - 1) / blocks_per_page - id0 + 1;
+        for (int i = threadIdx.x; i < n_ids; i += kThreads) {
+            int page = -1;
+            if (id0 + i < n_pages) page = pages[id0 + i];
+            ids[i] = (page >= 0 && page < num_pages) ? page : -1;
         }
-        auto iteration = [&](int jt, char *cur, char *nxt) {
-            const bool more = jt + 2 < tile_end;
-            if (more) dma_pair(nxt, jt + 2);
-            compute(cur, jt);
-            __syncthreads();
-            if (more && edge_pair(jt + 2)) {
-                fixup_pair(nxt, jt + 2);
-                __syncthreads();
-            }
-        };
-        int jt = tile_beg;
-        for (; jt + 2 < tile_end; jt += 4) {
-            iteration(jt, stage0, stage1);
-            iteration(jt + 2, stage1, stage0);
+        __syncthreads();   // also publishes Q^T on the first pass
+        Ops a, b;
+        int blk = pass_beg + wave;
+        fetch_k(a, blk);
+        fetch_v(a, blk);
+        for (; blk < pass_end; blk += 2 * kWaves) {
+            fetch_k(b, blk + kWaves);
+            compute(a, blk, b, blk + kWaves);
+            fetch_k(a, blk + 2 * kWaves);
+            compute(b, blk + kWaves, a, blk + 2 * kWaves);
         }
-        if (jt < tile_end) iteration(jt, stage0, stage1);
+        __syncthreads();   // the ids are rewritten by the next pass
     }
+    if (blk_beg >= blk_end) __syncthreads();   // Q^T's stores land before the combine's
 
-    // Combine the four waves' partial softmax states through LDS (the ring is
-    // free: the last barrier has passed). Wave w's row c: [D] outputs, m, l.
+    // Combine the four waves' partial softmax states through LDS (the last
+    // pass's barrier has every wave done with Q^T there).
     const float ltot = sum_halves(lsum);
-    float *cbuf = reinterpret_cast<float *>(wave < 2 ? stage0 : stage1) + (wave & 1) * kWaveRows * kLd;
+    float *mine = cbuf + wave * kWaveRows * kLd;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            *reinterpret_cast<f32x4 *>(cbuf + col * kLd + 32 * db + 8 * jj + 4 * half) =
+            *reinterpret_cast<f32x4 *>(mine + col * kLd + 32 * db + 8 * jj + 4 * half) =
                 f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
     if (half == 0) {
-        cbuf[col * kLd + D] = m;
-        cbuf[col * kLd + D + 1] = ltot;
+        mine[col * kLd + D] = m;
+        mine[col * kLd + D + 1] = ltot;
     }
     __syncthreads();
 
-    // 8 threads per column, D / 8 outputs each.
-    constexpr int kPer = D / 8;
+    constexpr int kPer = D / 8;   // 8 threads per column, D / 8 outputs each
     const int c = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * kPer;
-    const float *w0 = reinterpret_cast<const float *>(stage0), *w2 = reinterpret_cast<const float *>(stage1);
-    const float *src[4] = {w0 + c * kLd, w0 + (kWaveRows + c) * kLd, w2 + c * kLd, w2 + (kWaveRows + c) * kLd};
     float mmax = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mmax = fmaxf(mmax, src[w][D]);
-    float wgt[4], l = 0.f;
+    for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, cbuf[(w * kWaveRows + c) * kLd + D]);
+    float wgt[kWaves], l = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        wgt[w] = __builtin_amdgcn_exp2f(src[w][D] - mmax);
-        l += wgt[w] * src[w][D + 1];
+    for (int w = 0; w < kWaves; ++w) {
+        wgt[w] = __builtin_amdgcn_exp2f(cbuf[(w * kWaveRows + c) * kLd + D] - mmax);
+        l += wgt[w] * cbuf[(w * kWaveRows + c) * kLd + D + 1];
     }
     f32x4 acc[kPer / 4];
 #pragma unroll
     for (int i = 0; i < kPer / 4; ++i) {
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[i] += wgt[w] * *reinterpret_cast<const f32x4 *>(src[w] + d0 + 4 * i);
+        for (int w = 0; w < kWaves; ++w)
+            acc[i] += wgt[w] * *reinterpret_cast<const f32x4 *>(cbuf + (w * kWaveRows + c) * kLd + d0 + 4 * i);
     }
     const int cr = c / unit_heads, ch = c % unit_heads;
     if (c >= unit_rows * unit_heads || row0 + cr >= n_q || head0 + ch >= hq) return;
@@ -1158,8 +1161,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
     if (row >= total_q_rows) return;
     const int hd = head0 + ch;
     if (part >= 0) {
-        // Split unit: its combined unnormalised O, maximum and sum go to the
-        // workspace slot, pair r = (head offset) * unit_rows + (row offset).
         const int pairs = unit_rows * unit_heads, r = ch * unit_rows + cr;
         float *slot = parts + static_cast<int64_t>(part) * pairs * (D + 2);
 #pragma unroll
@@ -1361,16 +1362,20 @@ __global__ void fill_zero_kernel(float *__restrict__ x, int64_t n)
         x[i] = 0.f;
 }
 
-// Merge pass for split blocks (split-KV): one workgroup per merge entry, two
-// lanes per (query row, head) pair, each lane half of the head dim. The runs'
-// partial results combine exactly as blocks of one online softmax:
+// Merge pass for split blocks (split-KV): one workgroup per merge entry. The
+// runs' partial results combine exactly as blocks of one online softmax:
 // O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
+// First the workgroup reduces (M, L) of every valid (row, head) pair, several
+// lanes per pair each over a stride of the runs; then every lane owns four
+// consecutive dims of one pair and sums the runs' weighted O_r, so a wave reads
+// whole rows of the partial results and the loads of successive runs overlap.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
     const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
     const float *__restrict__ parts, int32_t num_parts, int32_t unit_rows, int32_t unit_heads,
     int32_t total_q_rows, int32_t hq, void *__restrict__ o, float *__restrict__ lse)
 {
+    __shared__ float red_m[kThreads], red_l[kThreads], fin_m[kThreads], fin_l[kThreads];
     const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
     const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
     const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
@@ -1378,46 +1383,68 @@ __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
     const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
     const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q];
     const int pairs = unit_rows * unit_heads;
+    const int rows_ok = min(unit_rows, n_q - row0), heads_ok = min(unit_heads, hq - head0);
+    const int nv = rows_ok * heads_ok;   // valid pairs, vr = head-major over rows_ok
+    if (rows_ok < 1 || heads_ok < 1 || pairs > kThreads) return;
     const int64_t kSlot = static_cast<int64_t>(pairs) * (D + 2);   // floats per partial result
-    constexpr int kHalf = D / 2;
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    for (int item = threadIdx.x; item < 2 * pairs; item += kThreads) {
-        const int r = item >> 1, half = item & 1;
-        const int head = head0 + r / unit_rows, t = row0 + r % unit_rows;
-        if (t >= n_q || head >= hq) continue;
-        const int64_t row = static_cast<int64_t>(q_row0) + t;
-        if (row >= total_q_rows) continue;
-        const float *base = parts + static_cast<int64_t>(part0) * kSlot;
-        float mmax = kNegBig;
-        for (int p = 0; p < nparts; ++p) mmax = fmaxf(mmax, base[p * kSlot + pairs * D + r]);
-        f32x4 acc[kHalf / 4];
-#pragma unroll
-        for (int i = 0; i < kHalf / 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float l = 0.f;
-        for (int p = 0; p < nparts; ++p) {
-            const float *slot = base + p * kSlot;
-            const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - mmax);
-            l += w * slot[pairs * (D + 1) + r];
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + half * kHalf);
-#pragma unroll
-            for (int i = 0; i < kHalf / 4; ++i) acc[i] += w * src[i];
-        }
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        const int64_t obase = (row * hq + head) * D + half * kHalf;
-#pragma unroll
-        for (int i = 0; i < kHalf / 4; ++i) {
-            const f32x4 v = acc[i] * inv;
-            if constexpr (OUT_BF16) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + 4 * i) =
-                    bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                           static_cast<__bf16>(v[3])};
-            } else {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + 4 * i) = v;
+    const float *base = parts + static_cast<int64_t>(part0) * kSlot;
+    auto slot_pair = [&](int vr) { return (vr / rows_ok) * unit_rows + vr % rows_ok; };
+
+    // (M, L) per valid pair: kThreads / nv lanes per pair, combined in LDS.
+    const int per = kThreads / nv, i = threadIdx.x;
+    {
+        float M = kNegBig, L = 0.f;
+        if (i < per * nv) {
+            const int r = slot_pair(i % nv);
+            for (int p = i / nv; p < nparts; p += per) {
+                const float mp = base[p * kSlot + pairs * D + r], lp = base[p * kSlot + pairs * (D + 1) + r];
+                const float mn = fmaxf(M, mp);
+                L = L * __builtin_amdgcn_exp2f(M - mn) + lp * __builtin_amdgcn_exp2f(mp - mn);
+                M = mn;
             }
         }
-        if (lse && half == 0)
-            lse[static_cast<int64_t>(head) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+        red_m[i] = M;
+        red_l[i] = L;
+    }
+    __syncthreads();
+    if (i < nv) {
+        float M = kNegBig, L = 0.f;
+        for (int g = 0; g < per; ++g) M = fmaxf(M, red_m[g * nv + i]);
+        for (int g = 0; g < per; ++g) L += red_l[g * nv + i] * __builtin_amdgcn_exp2f(red_m[g * nv + i] - M);
+        fin_m[i] = M;
+        fin_l[i] = L;
+    }
+    __syncthreads();
+
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kChunks = D / 4;
+    for (int item = i; item < nv * kChunks; item += kThreads) {
+        const int vr = item / kChunks, ch = item % kChunks;
+        const int r = slot_pair(vr);
+        const int head = head0 + vr / rows_ok, t = row0 + vr % rows_ok;
+        const int64_t row = static_cast<int64_t>(q_row0) + t;
+        if (row >= total_q_rows) continue;
+        const float M = fin_m[vr], l = fin_l[vr];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int p = 0; p < nparts; ++p) {
+            const float *slot = base + p * kSlot;
+            const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - M);
+            acc += w * *reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + 4 * ch);
+        }
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const f32x4 v = acc * inv;
+        const int64_t obase = (row * hq + head) * D + 4 * ch;
+        if constexpr (OUT_BF16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase) =
+                bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                       static_cast<__bf16>(v[3])};
+        } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase) = v;
+        }
+        if (lse && ch == 0)
+            lse[static_cast<int64_t>(head) * total_q_rows + row] = (M + __log2f(l)) * 0.69314718055994530942f;
     }
 }
 

@@ -48,9 +48,9 @@ inline bool decode_units(int G, int page_size, int max_new_rows)
     return page_size >= kKvTile && G <= kWaveRows && max_new_rows <= kWaveRows / G;
 }
 inline UnitShape decode_shape(int G) { return UnitShape{kWaveRows / G, G}; }
-// Workgroup slots of the decode kernel (one per CU) and the work units per
+// Workgroup slots of the decode kernel (two per CU) and the work units per
 // slot its split-KV policy aims at.
-constexpr int kDecodeSlots = 256;
+constexpr int kDecodeSlots = 512;
 constexpr int kDecodeUnitsPerSlot = 4;
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
