@@ -891,15 +891,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
 // Decode / small-chunk kernel (pages of at least one tile). A unit is one
 // segment's few new rows for all G query heads of its KV head: column c of
 // the MFMAs is the (row c / G, head c % G) pair, so the 32 columns carry up to
-// 32 / G rows. The step is bound by HBM bandwidth, so the kernel is built to
-// keep bytes in flight: every wavefront streams its own 32-key blocks of the
-// unit's run (blocks w, w + 4, ...) straight into its MFMA operand registers,
-// loading the next block while it computes the current one, with no LDS and
-// no barrier in the loop; two workgroups per CU. Each wave keeps its own
-// running maximum, sum and O^T; at the end the four combine through LDS as
-// blocks of one online softmax.
+// 32 / G rows. The step is bound by HBM bandwidth. Each workgroup is a single
+// wavefront that streams its unit's 32-key blocks straight from the pages into
+// its MFMA operand registers, loading the next block while it computes the
+// current one; eight such workgroups share a CU, so one wave's start (reading
+// its unit's descriptors, Q and page ids) and finish (writing its result)
+// overlap the other waves' streaming, and no wave waits for another.
+constexpr int kDecThreads = 64;
+
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
+__global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
     int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
@@ -908,9 +909,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
 {
     constexpr int kSteps = D / 16;
     constexpr int kDBlocks = D / 32;
-    constexpr int kLd = D + 4;   // floats per (wave, column) row of the combine buffer
-    constexpr int kBlock = 32;   // keys per block
-    __shared__ __attribute__((aligned(16))) float cbuf[kWaves * kWaveRows * kLd];
+    constexpr int kQLd = D + 8;    // bf16 per Q^T column row: 16-byte pad, so the lanes' reads hit distinct banks
+    constexpr int kIdCap = 1024;   // page ids staged per pass
+    __shared__ __attribute__((aligned(16))) u16 qlds[kWaveRows * kQLd];
+    __shared__ int32_t ids[kIdCap];
 
     const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
     const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
     const int page_off = desc[SEGKV_SEG_PAGE_OFF];
-    // k_pos0 starts a page, so a 32-key block never crosses one.
+    // k_pos0 starts a page, so a 64-key tile never crosses one.
     if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1 ||
         (k_pos0 & ((1 << log2P) - 1)) != 0)
         return;
@@ -934,16 +936,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const int32_t *pages = page_list + page_off;
     const int P = 1 << log2P;
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     const int col = lane & 31, half = lane >> 5;
 
-    // Rows of the unit and its band of tiles, cut to the unit's run; in 32-key blocks.
+    // Rows of the unit and its band of tiles, cut to the unit's run.
     const int unit_end = min(row0 + unit_rows, n_q);
     const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
     const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
     const int tile_beg = max((lo_pos - k_pos0) / kBK, run0);
     const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
-    const int blk_beg = 2 * tile_beg, blk_end = 2 * tile_end;
     const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);   // stored and visible keys
     const int zero_hi = k_len;
 
@@ -957,13 +958,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const int all_lo = max(window ? last_pos - window + 1 : 0, run_lo);
     const int all_hi = min(first_pos, run_hi);
 
-    // Q^T (the B operand, lane column = pair) sits in LDS for the loop, in the
-    // combine buffer's space, rows padded by 16 bytes so the lanes' 16-byte
-    // reads fall in distinct banks.
-    constexpr int kQLd = D + 8;   // bf16 per column row
-    static_assert(kWaveRows * kQLd * 2 <= static_cast<int>(sizeof(cbuf)), "Q^T must fit the combine buffer");
-    u16 *qlds = reinterpret_cast<u16 *>(cbuf);
-    for (int i = threadIdx.x; i < kWaveRows * (D / 8); i += kThreads) {
+    // Q^T, the B operand (lane column = pair), sits in LDS for the loop.
+    for (int i = lane; i < kWaveRows * (D / 8); i += kDecThreads) {
         const int qc = i / (D / 8), qd = 8 * (i % (D / 8));
         const int qr = qc / unit_heads, qh = qc % unit_heads;
         u32x4 raw = {0u, 0u, 0u, 0u};
@@ -979,96 +975,89 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
     float m = kNegBig, lsum = 0.f;
 
-    // Page ids of the run, staged in LDS after Q^T a pass of kIdCap pages at a
-    // time (k_pos0 starts a page, so entry e holds keys e P .. e P + P - 1).
-    constexpr int kIdCap = 4096;
-    static_assert(kWaveRows * kQLd * 2 + kIdCap * 4 <= static_cast<int>(sizeof(cbuf)), "page ids must fit");
-    int32_t *ids = reinterpret_cast<int32_t *>(cbuf + kWaveRows * kQLd / 2);
-    const int blocks_per_page = P / kBlock;
-    const int blocks_per_pass = kIdCap * blocks_per_page;
+    // Page ids of the run, staged in LDS a pass of kIdCap pages at a time
+    // (k_pos0 starts a page, so entry e holds keys e P .. e P + P - 1).
+    const int tiles_per_page = P / kBK;
+    const int tiles_per_pass = kIdCap * tiles_per_page;
 
-    // Operands of one 32-key block, read from its page with buffer loads (a
-    // missing page or a block past the pass has an empty range: zeros, no
-    // traffic, and every path issues the same loads, so the waits the compiler
-    // places before using a block count only that block's loads). K: the A
-    // operand of S^T = K . Q^T, lane row swizzle_row(col) (so S^T registers are
-    // the P^T operand), 8 dims at 16 s + 8 half. V^T: the A operand of
+    // One 64-key tile's operands, read from its page with buffer loads (a
+    // missing page or a tile past the pass has an empty range: zeros, no
+    // traffic; every path issues the same loads, so the compiler's waits
+    // before a use count only that tile's loads). Each batch of V loads covers
+    // whole 128-byte lines of the V^T rows: reading the two halves of a line
+    // far apart in time costs HBM efficiency. K: the A operand of
+    // S^T = K . Q^T for keys 32 g + swizzle_row(col) (so S^T registers are the
+    // P^T operand), 8 dims at 16 s + 8 half. V^T: the A operand of
     // O^T += V^T . P^T, row d = 32 db + col, keys 16 t + 8 half .. + 7.
-    struct Ops {
-        bf16x8 k[kSteps];
-        bf16x8 v[2][kDBlocks];
-    };
+    bf16x8 kreg[2][kSteps];
+    bf16x8 vreg[4][kDBlocks];
     const unsigned k_lane = static_cast<unsigned>((swizzle_row(col) * D + 8 * half) * 2);
     const unsigned v_lane = static_cast<unsigned>((col * P + 8 * half) * 2);
-    int pass_beg = blk_beg, pass_end = blk_beg, id0 = 0;
-    auto page_of = [&](int blk) -> int {
+    int pass_end = 0, id0 = 0;
+    auto page_of = [&](int tile) -> int {
         int page = -1;
-        if (blk < pass_end) page = __builtin_amdgcn_readfirstlane(ids[blk / blocks_per_page - id0]);
+        if (tile < pass_end) page = __builtin_amdgcn_readfirstlane(ids[tile / tiles_per_page - id0]);
         return page;
     };
-    auto fetch_k = [&](Ops &op, int blk) {
-        const int page = page_of(blk);
+    auto fetch_k = [&](int tile) {
+        const int page = page_of(tile);
         const int pg = max(page, 0);
         const __amdgpu_buffer_rsrc_t rk =
             page_rsrc(kpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
-        const unsigned off = k_lane + static_cast<unsigned>(((blk * kBlock) & (P - 1)) * D * 2);
+        const unsigned off = k_lane + static_cast<unsigned>(((tile * kBK) & (P - 1)) * D * 2);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-            op.k[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 32 * s, 0, 0));
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s)
+                kreg[g][s] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 32 * g * D * 2 + 32 * s, 0, 0));
     };
-    auto fetch_v = [&](Ops &op, int blk) {
-        const int page = page_of(blk);
+    auto fetch_v = [&](int tile) {
+        const int page = page_of(tile);
         const int pg = max(page, 0);
         const __amdgpu_buffer_rsrc_t rv =
             page_rsrc(vpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
-        const unsigned off = v_lane + static_cast<unsigned>(((blk * kBlock) & (P - 1)) * 2);
+        const unsigned off = v_lane + static_cast<unsigned>(((tile * kBK) & (P - 1)) * 2);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-            for (int db = 0; db < kDBlocks; ++db)
-                op.v[t][db] = __builtin_bit_cast(
+            for (int t = 0; t < 4; ++t)
+                vreg[t][db] = __builtin_bit_cast(
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off + 64 * db * P + 32 * t, 0, 0));
     };
 
-    // One block; the next block's V is requested once this block's K is used.
-    auto compute = [&](Ops &op, int blk, Ops &nxt, int nxt_blk) {
-        const int key0 = blk * kBlock;
-        // V entries outside the stored-and-visible range may hold anything
-        // (0 * NaN would reach O): clear them on the blocks that have any.
-        if (key0 < zero_lo || key0 + kBlock > zero_hi) {
+    // One tile: S^T, then the next tile's K is requested; the softmax; P V,
+    // then the next tile's V is requested.
+    auto compute = [&](int tile) {
+        const int key0 = tile * kBK;
+        f32x16 sacc[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                u32x4 keep;
+        for (int g = 0; g < 2; ++g) {
+            sacc[g] = f32x16{};
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int idx = key0 + 16 * t + 8 * half + 2 * w;
-                    keep[w] = ((idx >= zero_lo && idx < zero_hi) ? 0xffffu : 0u) |
-                              ((idx + 1 >= zero_lo && idx + 1 < zero_hi) ? 0xffff0000u : 0u);
-                }
-#pragma unroll
-                for (int db = 0; db < kDBlocks; ++db)
-                    op.v[t][db] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, op.v[t][db]) & keep);
-            }
+            for (int s = 0; s < kSteps; ++s)
+                sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    kreg[g][s], *reinterpret_cast<const bf16x8 *>(qcol + 16 * s), sacc[g], 0, 0, 0);
         }
-        f32x16 sacc = {};
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                op.k[s], *reinterpret_cast<const bf16x8 *>(qcol + 16 * s), sacc, 0, 0, 0);
-        fetch_v(nxt, nxt_blk);
+        fetch_k(tile + 1);
         const int kp0 = k_pos0 + key0;
-        const bool live = blk < pass_end;   // a block past the pass belongs to the next one
-        if (!(live && kp0 >= all_lo && kp0 + kBlock - 1 <= all_hi)) {
-            const int kbase = kp0 + 8 * half;
+        const bool live = tile < pass_end;   // a tile past the pass belongs to the next one
+        if (!(live && kp0 >= all_lo && kp0 + kBK - 1 <= all_hi)) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int pos = kbase + 16 * (e >> 3) + (e & 7);
-                sacc[e] = (live && pos >= lo_eff && pos <= hi_eff) ? sacc[e] : -__builtin_inff();
+            for (int g = 0; g < 2; ++g) {
+                const int kbase = kp0 + 32 * g + 8 * half;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int pos = kbase + 16 * (e >> 3) + (e & 7);
+                    sacc[g][e] = (live && pos >= lo_eff && pos <= hi_eff) ? sacc[g][e] : -__builtin_inff();
+                }
             }
         }
-        float mx = vmax(sacc[0], sacc[1]);
+        float mx = vmax(sacc[0][0], sacc[0][1]);
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) mx = vmax(vmax(mx, sacc[e]), sacc[e + 1]);
+        for (int e = 2; e < 16; e += 2) mx = vmax(vmax(mx, sacc[0][e]), sacc[0][e + 1]);
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mx = vmax(vmax(mx, sacc[1][e]), sacc[1][e + 1]);
         const float mt = max_halves(mx) * scale_log2;
         if (__any(mt > m + kRescaleSlack)) {
             const float m_new = fmaxf(m, mt);
@@ -1078,115 +1067,99 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
             for (int i = 0; i < kDBlocks; ++i) oacc[i] *= alpha;
             m = m_new;
         }
+        // V entries outside the stored-and-visible range may hold anything
+        // (0 * NaN would reach O): clear them on the tiles that have any.
+        if (key0 < zero_lo || key0 + kBK > zero_hi) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 4; ++t) {
+                u32x4 keep;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int idx = key0 + 16 * t + 8 * half + 2 * w;
+                    keep[w] = ((idx >= zero_lo && idx < zero_hi) ? 0xffffu : 0u) |
+                              ((idx + 1 >= zero_lo && idx + 1 < zero_hi) ? 0xffff0000u : 0u);
+                }
+#pragma unroll
+                for (int db = 0; db < kDBlocks; ++db)
+                    vreg[t][db] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vreg[t][db]) & keep);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
             bf16x8 pb;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * t + i], scale_log2, -m)));
+                pb[i] = static_cast<__bf16>(
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][8 * (t & 1) + i], scale_log2, -m)));
             lsum = sum8_bf16(pb, lsum);
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v[t][db], pb, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vreg[t][db], pb, oacc[db], 0, 0, 0);
         }
+        fetch_v(tile + 1);
     };
 
-    // Passes over the pages of each kIdCap-page stretch of the segment; in
-    // each, wave w takes blocks w, w + 4, ... two at a time (a block past the
-    // pass is all masked and reads nothing), the next block loading while one
-    // computes.
-    for (; pass_beg < blk_end; pass_beg = pass_end) {
-        pass_end = min(blk_end, (pass_beg / blocks_per_pass + 1) * blocks_per_pass);
-        id0 = pass_beg / blocks_per_page;
-        const int n_ids = (pass_end - 1) / blocks_per_page - id0 + 1;
-        for (int i = threadIdx.x; i < n_ids; i += kThreads) {
+    // Passes over the pages of each kIdCap-page stretch of the segment, one
+    // tile per step (the tile past a pass is requested as an empty range).
+    for (int pass_beg = tile_beg; pass_beg < tile_end; pass_beg = pass_end) {
+        pass_end = min(tile_end, (pass_beg / tiles_per_pass + 1) * tiles_per_pass);
+        id0 = pass_beg / tiles_per_page;
+        const int n_ids = (pass_end - 1) / tiles_per_page - id0 + 1;
+        for (int i = lane; i < n_ids; i += kDecThreads) {
             int page = -1;
             if (id0 + i < n_pages) page = pages[id0 + i];
             ids[i] = (page >= 0 && page < num_pages) ? page : -1;
         }
-        __syncthreads();   // also publishes Q^T on the first pass
-        Ops a, b;
-        int blk = pass_beg + wave;
-        fetch_k(a, blk);
-        fetch_v(a, blk);
-        for (; blk < pass_end; blk += 2 * kWaves) {
-            fetch_k(b, blk + kWaves);
-            compute(a, blk, b, blk + kWaves);
-            fetch_k(a, blk + 2 * kWaves);
-            compute(b, blk + kWaves, a, blk + 2 * kWaves);
-        }
-        __syncthreads();   // the ids are rewritten by the next pass
+        __syncthreads();   // the ids (and on the first pass Q^T) are visible to every lane
+        fetch_k(pass_beg);
+        fetch_v(pass_beg);
+        for (int tile = pass_beg; tile < pass_end; ++tile) compute(tile);
+        __syncthreads();   // every lane is done with the ids before the next pass rewrites them
     }
-    if (blk_beg >= blk_end) __syncthreads();   // Q^T's stores land before the combine's
 
-    // Combine the four waves' partial softmax states through LDS (the last
-    // pass's barrier has every wave done with Q^T there).
+    // Results straight from the O^T registers: lane (col, half) holds dims
+    // 32 db + 8 j + 4 half + i of pair col as oacc[db][4 j + i].
     const float ltot = sum_halves(lsum);
-    float *mine = cbuf + wave * kWaveRows * kLd;
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            *reinterpret_cast<f32x4 *>(mine + col * kLd + 32 * db + 8 * jj + 4 * half) =
-                f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
-    if (half == 0) {
-        mine[col * kLd + D] = m;
-        mine[col * kLd + D + 1] = ltot;
-    }
-    __syncthreads();
-
-    constexpr int kPer = D / 8;   // 8 threads per column, D / 8 outputs each
-    const int c = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * kPer;
-    float mmax = kNegBig;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, cbuf[(w * kWaveRows + c) * kLd + D]);
-    float wgt[kWaves], l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        wgt[w] = __builtin_amdgcn_exp2f(cbuf[(w * kWaveRows + c) * kLd + D] - mmax);
-        l += wgt[w] * cbuf[(w * kWaveRows + c) * kLd + D + 1];
-    }
-    f32x4 acc[kPer / 4];
-#pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) {
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            acc[i] += wgt[w] * *reinterpret_cast<const f32x4 *>(cbuf + (w * kWaveRows + c) * kLd + d0 + 4 * i);
-    }
-    const int cr = c / unit_heads, ch = c % unit_heads;
-    if (c >= unit_rows * unit_heads || row0 + cr >= n_q || head0 + ch >= hq) return;
+    const int cr = col / unit_heads, ch = col % unit_heads;
+    if (col >= unit_rows * unit_heads || row0 + cr >= n_q || head0 + ch >= hq) return;
     const int64_t row = static_cast<int64_t>(q_row0) + row0 + cr;
     if (row >= total_q_rows) return;
     const int hd = head0 + ch;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     if (part >= 0) {
         const int pairs = unit_rows * unit_heads, r = ch * unit_rows + cr;
         float *slot = parts + static_cast<int64_t>(part) * pairs * (D + 2);
 #pragma unroll
-        for (int i = 0; i < kPer / 4; ++i) *reinterpret_cast<f32x4 *>(slot + r * D + d0 + 4 * i) = acc[i];
-        if ((threadIdx.x & 7) == 0) {
-            slot[pairs * D + r] = mmax;
-            slot[pairs * (D + 1) + r] = l;
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4 *>(slot + r * D + 32 * db + 8 * j + 4 * half) =
+                    f32x4{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+        if (half == 0) {
+            slot[pairs * D + r] = m;
+            slot[pairs * (D + 1) + r] = ltot;
         }
         return;
     }
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t obase = (row * hq + hd) * D + d0;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    const int64_t obase = (row * hq + hd) * D + 4 * half;
 #pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) {
-        const f32x4 v = acc[i] * inv;
-        if constexpr (OUT_BF16) {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + 4 * i) =
-                bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                       static_cast<__bf16>(v[3])};
-        } else {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + 4 * i) = v;
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 v = f32x4{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]} * inv;
+            const int64_t at = obase + 32 * db + 8 * j;
+            if constexpr (OUT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + at) =
+                    bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                           static_cast<__bf16>(v[3])};
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + at) = v;
+            }
         }
-    }
-    if (lse && (threadIdx.x & 7) == 0)
-        lse[static_cast<int64_t>(hd) * total_q_rows + row] = (mmax + __log2f(l)) * 0.69314718055994530942f;
+    if (lse && half == 0)
+        lse[static_cast<int64_t>(hd) * total_q_rows + row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
 // Attention mass of the step's new tokens (RedKnot summary page, "Sparse
@@ -1362,20 +1335,26 @@ __global__ void fill_zero_kernel(float *__restrict__ x, int64_t n)
         x[i] = 0.f;
 }
 
-// Merge pass for split blocks (split-KV): one workgroup per merge entry. The
-// runs' partial results combine exactly as blocks of one online softmax:
+// Merge pass for split blocks (split-KV): kMergeDSplit workgroups per merge
+// entry, each for a quarter of the head dim. The runs' partial results
+// combine exactly as blocks of one online softmax:
 // O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
 // First the workgroup reduces (M, L) of every valid (row, head) pair, several
-// lanes per pair each over a stride of the runs; then every lane owns four
-// consecutive dims of one pair and sums the runs' weighted O_r, so a wave reads
-// whole rows of the partial results and the loads of successive runs overlap.
+// lanes per pair each over a stride of the runs; then each lane owns four
+// consecutive dims of one pair and sums the weighted O_r of a stride of the
+// runs (few pairs: several lanes per item, added up in LDS), so a wave reads
+// whole rows of the partial results and the loads of many runs overlap.
+constexpr int kMergeDSplit = 4;
+
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
     const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
     const float *__restrict__ parts, int32_t num_parts, int32_t unit_rows, int32_t unit_heads,
     int32_t total_q_rows, int32_t hq, void *__restrict__ o, float *__restrict__ lse)
 {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ float red_m[kThreads], red_l[kThreads], fin_m[kThreads], fin_l[kThreads];
+    __shared__ f32x4 red_o[kThreads];
     const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
     const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
     const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
@@ -1416,22 +1395,38 @@ __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
     }
     __syncthreads();
 
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int kChunks = D / 4;
-    for (int item = i; item < nv * kChunks; item += kThreads) {
-        const int vr = item / kChunks, ch = item % kChunks;
+    // This workgroup's dims: chunks [c0, c0 + kChunks) of four.
+    constexpr int kChunks = D / 4 / kMergeDSplit;
+    const int c0 = static_cast<int>(blockIdx.y) * kChunks;
+    const int items = nv * kChunks;
+    const int groups = items < kThreads ? kThreads / items : 1;   // lanes per item, each over a stride of runs
+    const int grp = i / (items < kThreads ? items : kThreads);
+    for (int item0 = 0; item0 < items; item0 += kThreads) {
+        const int item = item0 + (groups > 1 ? i % items : i);
+        const bool mine = item < items && grp < groups;
+        const int vr = mine ? item / kChunks : 0, ch = c0 + (mine ? item % kChunks : 0);
         const int r = slot_pair(vr);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (mine) {
+            const float M = fin_m[vr];
+#pragma unroll 8
+            for (int p = grp; p < nparts; p += groups) {
+                const float *slot = base + p * kSlot;
+                const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - M);
+                acc += w * *reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + 4 * ch);
+            }
+        }
+        if (groups > 1) {
+            red_o[i] = acc;
+            __syncthreads();
+            if (grp == 0)
+                for (int g = 1; g < groups; ++g) acc += red_o[g * items + i];
+        }
+        if (!mine || grp != 0) continue;
         const int head = head0 + vr / rows_ok, t = row0 + vr % rows_ok;
         const int64_t row = static_cast<int64_t>(q_row0) + t;
         if (row >= total_q_rows) continue;
         const float M = fin_m[vr], l = fin_l[vr];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int p = 0; p < nparts; ++p) {
-            const float *slot = base + p * kSlot;
-            const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - M);
-            acc += w * *reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + 4 * ch);
-        }
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         const f32x4 v = acc * inv;
         const int64_t obase = (row * hq + head) * D + 4 * ch;
@@ -1464,10 +1459,10 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
     const u16 *vp = static_cast<const u16 *>(cfg.v_pool);
     const int log2P = log2_of(cfg.page_size);
     if (cfg.page_size >= kBK && t.unit_rows * t.unit_heads <= kWaveRows)
-        hipLaunchKernelGGL((attn_decode_kernel<D, OUT_BF16>), grid, block, 0, stream, qh, kp, vp, cfg.num_pages,
-                           log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
-                           t.total_q_rows, cfg.num_q_heads, t.unit_rows, t.unit_heads, scale_log2, o, lse, parts,
-                           t.num_parts);
+        hipLaunchKernelGGL((attn_decode_kernel<D, OUT_BF16>), grid, dim3(kDecThreads), 0, stream, qh, kp, vp,
+                           cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
+                           t.num_segments, t.total_q_rows, cfg.num_q_heads, t.unit_rows, t.unit_heads, scale_log2,
+                           o, lse, parts, t.num_parts);
     else if (cfg.page_size >= kBK)
         hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16>), grid, block, 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
@@ -1477,8 +1472,8 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse);
     if (t.num_merges > 0)
-        hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges)), block, 0,
-                           stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_rows,
+        hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges), kMergeDSplit),
+                           block, 0, stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_rows,
                            t.unit_heads, t.total_q_rows, cfg.num_q_heads, o, lse);
 }
 

@@ -48,10 +48,12 @@ inline bool decode_units(int G, int page_size, int max_new_rows)
     return page_size >= kKvTile && G <= kWaveRows && max_new_rows <= kWaveRows / G;
 }
 inline UnitShape decode_shape(int G) { return UnitShape{kWaveRows / G, G}; }
-// Workgroup slots of the decode kernel (two per CU) and the work units per
-// slot its split-KV policy aims at.
-constexpr int kDecodeSlots = 512;
-constexpr int kDecodeUnitsPerSlot = 4;
+// Workgroup slots of the decode kernel (eight single-wave workgroups per CU),
+// the work units per slot its split-KV policy aims at, and the shortest run
+// (in 64-key tiles) it cuts a block into.
+constexpr int kDecodeSlots = 2048;
+constexpr int kDecodeUnitsPerSlot = 1;
+constexpr int kDecodeMinRun = 8;
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_page_size(int p) { return p == 16 || p == 32 || p == 64 || p == 128 || p == 256; }

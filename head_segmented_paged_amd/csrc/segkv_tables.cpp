@@ -149,8 +149,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
             // Decode: a handful of long blocks; cut them into enough even runs
             // for several units per workgroup slot.
             const int64_t target = static_cast<int64_t>(segkv::kDecodeSlots) * segkv::kDecodeUnitsPerSlot;
-            max_run = std::max<int64_t>(segkv::kMinRun / 2, (total_tiles + target - 1) / target);
-            max_run += max_run & 1;
+            max_run = std::max<int64_t>(segkv::kDecodeMinRun, (total_tiles + target - 1) / target);
         } else {
             const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::kCohort;
             if (4 * longest * slots > 3 * total_tiles)
