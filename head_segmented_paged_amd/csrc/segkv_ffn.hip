@@ -143,13 +143,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kGemmThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kTileBytes = kBM * kBK * 2;   // one 128 x 64 bf16 operand tile, 16 KB
-constexpr int kRowBytes = kBK * 2;          // 128 B per tile row
+constexpr int kGemmThreads = 512;                 // eight waves, two per SIMD
+constexpr int kBM = 256;                    // A rows (chosen tokens) per tile
+constexpr int kBN = 128;                    // output columns per tile
+constexpr int kBK = 32;                     // K per stage
+constexpr int kRowBytes = kBK * 2;          // 64 B per tile row
+constexpr int kATileBytes = kBM * kRowBytes;   // 16 KB
 
-// Row r of a tile keeps its 16-byte chunk c at position c ^ gswz(r).
-__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
+// Row r of a tile keeps its 16-byte chunk c at position c ^ gswz(r): sixteen
+// lanes reading one chunk of sixteen consecutive rows hit sixteen distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ void gdma16(__amdgpu_buffer_rsrc_t rsrc, char *lds, unsigned voffset, unsigned soffset)
 {
@@ -163,32 +167,63 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const u16 *base, int
                                              0x00020000);
 }
 
+// Wait until at most N of this wave's vector-memory operations (here: LDS
+// DMAs) are outstanding and all its LDS reads are done, then meet the other
+// waves. Unlike __syncthreads, which waits for every DMA, this leaves the
+// newer stages in flight.
+template <int N>
+__device__ __forceinline__ void wait_dma_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896340736f)); }
 
 // GATE: A = x rows chosen by rows[], B0 = Wg, B1 = Wu -> h. Otherwise A = h,
 // B0 = Wd -> x[rows[m]] += result.
+// A workgroup computes a 256 x 128 output tile (for GATE both the gate and the
+// up projection of it), eight waves of 64 x 64 each, two per SIMD. The tile
+// size sets how many bytes each MFMA needs from L2: 128 flops per byte staged
+// into LDS here, against 64-85 for 128 x 128 tiles. Operands stream through an
+// LDS ring of 32-wide K slices, all but one in flight while one is multiplied.
 template <bool GATE>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
     const u16 *__restrict__ a, int64_t a_bytes, const int32_t *__restrict__ rows, int64_t x_rows, int32_t M,
     int32_t K, const u16 *__restrict__ b0, const u16 *__restrict__ b1, int64_t b_bytes, int32_t N,
     u16 *__restrict__ out)
 {
-    constexpr int kTiles = GATE ? 3 : 2;                  // A, B0 (, B1)
-    __shared__ __attribute__((aligned(1024))) char st0[kTiles * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char st1[kTiles * kTileBytes];
+    constexpr int kBRows = GATE ? 2 * kBN : kBN;           // B tile rows: gate rows then up rows, or down rows
+    constexpr int kBTileBytes = kBRows * kRowBytes;
+    constexpr int kStage = kATileBytes + kBTileBytes;      // 32 KB or 24 KB
+    constexpr int kAInstr = kATileBytes / 1024 / 8;        // DMA instructions per wave and stage
+    constexpr int kBInstr = kBTileBytes / 1024 / 8;
+    constexpr int kInstr = kAInstr + kBInstr;
+    constexpr int kBCols = GATE ? 4 : 2;                   // 32-column B blocks per wave (gate 0, 1; up 2, 3)
+    // LDS ring of kStages stages (128 KB and 96 KB), indexed by constants
+    // only, so the compiler sees that a DMA into one stage does not alias the
+    // LDS reads of another and adds no wait for it. Five- and six-stage rings
+    // measured no faster.
+    constexpr int kStages = 4;
+    __shared__ __attribute__((aligned(1024))) char ring[kStages][kStage];
 
-    const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+    const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 3, wn = wave >> 2;
 
-    // DMA: each wave moves 4 KB of every tile per K chunk, 16 bytes a lane.
-    const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(a, a_bytes), rb0 = gemm_rsrc(b0, b_bytes);
-    const __amdgpu_buffer_rsrc_t rb1 = gemm_rsrc(GATE ? b1 : b0, b_bytes);
-    unsigned aoff[4], boff[4];
+    // DMA: every wave moves kInstr KB of each stage, 16 bytes a lane. A B-tile
+    // instruction covers 16 rows, all of one weight matrix: for GATE waves
+    // 0-3 fill the gate rows and waves 4-7 the up rows.
+    const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(a, a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(GATE && wave >= 4 ? b1 : b0, b_bytes);
+    const __amdgpu_buffer_rsrc_t rnone = gemm_rsrc(a, 0);   // empty range: the ring's tail DMAs read nothing
+    unsigned aoff[kAInstr], boff[kBInstr];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = (wave * 4 + i) * 1024 + lane * 16;
+    for (int i = 0; i < kAInstr; ++i) {
+        const int p = (wave * kAInstr + i) * 1024 + lane * 16;
         const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz(r);
         const int m = m0 + r;
         int64_t arow = -1;
@@ -197,75 +232,105 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
         // only output rows that are never written depend on it.
         if (arow < 0 || (GATE && arow >= x_rows)) arow = 0;
         aoff[i] = static_cast<unsigned>(arow * K * 2 + c * 16);
-        boff[i] = static_cast<unsigned>(static_cast<int64_t>(n0 + r) * K * 2 + c * 16);
     }
-    auto dma = [&](char *stage, int k0) {
-        const unsigned so = static_cast<unsigned>(k0 * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            char *dst = stage + (wave * 4 + i) * 1024;
-            gdma16(ra, dst, aoff[i], so);
-            gdma16(rb0, dst + kTileBytes, boff[i], so);
-            if constexpr (GATE) gdma16(rb1, dst + 2 * kTileBytes, boff[i], so);
-        }
+    for (int i = 0; i < kBInstr; ++i) {
+        const int p = (wave * kBInstr + i) * 1024 + lane * 16;
+        const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz(r);
+        const int wrow = n0 + (r % kBN);
+        boff[i] = static_cast<unsigned>(static_cast<int64_t>(wrow) * K * 2 + c * 16);
+    }
+    // Stage kc of the K loop; past the end the same count of DMAs reads an
+    // empty range (zeros into a stage nobody reads), so every wait below
+    // counts the same instructions.
+    const int chunks = K / kBK;
+    auto dma = [&](char *stage, int kc) {
+        const bool live = kc < chunks;
+        const unsigned so = live ? static_cast<unsigned>(kc * kBK * 2) : 0u;
+#pragma unroll
+        for (int i = 0; i < kAInstr; ++i) gdma16(live ? ra : rnone, stage + (wave * kAInstr + i) * 1024, aoff[i], so);
+#pragma unroll
+        for (int i = 0; i < kBInstr; ++i)
+            gdma16(live ? rb : rnone, stage + kATileBytes + (wave * kBInstr + i) * 1024, boff[i], so);
     };
 
-    // Operand addresses: A rows wm*64 + 32 bi + col, B rows wn*64 + 32 bj + col.
-    unsigned arow_lds[2], brow_lds[2];
+    // Operand rows: A rows wm * 64 + 32 i + col; B rows wn * 64 + 32 j + col
+    // (and the same plus kBN for the up rows).
+    unsigned arow_lds[2], brow_lds[kBCols];
+    int aswz[2], bswz[kBCols];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        arow_lds[i] = static_cast<unsigned>((wm * 64 + 32 * i + col) * kRowBytes);
-        brow_lds[i] = static_cast<unsigned>((wn * 64 + 32 * i + col) * kRowBytes);
+        const int r = wm * 64 + 32 * i + col;
+        arow_lds[i] = static_cast<unsigned>(r * kRowBytes);
+        aswz[i] = gswz(r);
     }
-    const int aswz[2] = {gswz(wm * 64 + col), gswz(wm * 64 + 32 + col)};
-    const int bswz[2] = {gswz(wn * 64 + col), gswz(wn * 64 + 32 + col)};
+#pragma unroll
+    for (int j = 0; j < kBCols; ++j) {
+        const int r = (j >> 1) * kBN + wn * 64 + 32 * (j & 1) + col;
+        brow_lds[j] = static_cast<unsigned>(kATileBytes + r * kRowBytes);
+        bswz[j] = gswz(r);
+    }
 
-    f32x16 acc0[2][2], acc1[2][2];
+    f32x16 acc[2][kBCols];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc0[i][j] = f32x16{};
-            acc1[i][j] = f32x16{};
-        }
+        for (int j = 0; j < kBCols; ++j) acc[i][j] = f32x16{};
 
+    struct Ops {
+        bf16x8 a[2], b[kBCols];
+    };
+    auto load_ops = [&](Ops &op, const char *stage, int s) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            op.a[i] = *reinterpret_cast<const bf16x8 *>(stage + arow_lds[i] + (((2 * s + half) ^ aswz[i]) << 4));
+#pragma unroll
+        for (int j = 0; j < kBCols; ++j)
+            op.b[j] = *reinterpret_cast<const bf16x8 *>(stage + brow_lds[j] + (((2 * s + half) ^ bswz[j]) << 4));
+    };
+    auto mfmas = [&](const Ops &op) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < kBCols; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a[i], op.b[j], acc[i][j], 0, 0, 0);
+    };
+    // The second k-step's operands are read while the first k-step's MFMAs
+    // run: the scheduling groups put one LDS read after each of the first
+    // MFMAs (the compiler would otherwise read each step's operands right
+    // before its MFMAs and leave the matrix core idle for the LDS latency).
     auto compute = [&](const char *stage) {
+        Ops x, y;
+        load_ops(x, stage, 0);
+        load_ops(y, stage, 1);
+        mfmas(x);
+        mfmas(y);
+        constexpr int kReads = 2 + kBCols, kMfma = 2 * kBCols;
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            bf16x8 av[2], bv[2], cv[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                av[i] = *reinterpret_cast<const bf16x8 *>(stage + arow_lds[i] + (((2 * s + half) ^ aswz[i]) << 4));
-                bv[i] = *reinterpret_cast<const bf16x8 *>(stage + kTileBytes + brow_lds[i] +
-                                                          (((2 * s + half) ^ bswz[i]) << 4));
-                if constexpr (GATE)
-                    cv[i] = *reinterpret_cast<const bf16x8 *>(stage + 2 * kTileBytes + brow_lds[i] +
-                                                              (((2 * s + half) ^ bswz[i]) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc0[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc0[i][j], 0, 0, 0);
-                    if constexpr (GATE)
-                        acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], cv[j], acc1[i][j], 0, 0, 0);
-                }
+        for (int r = 0; r < kReads; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfma - kReads, 0);
+    };
+    // Stage kc: wait for its DMA (the newer stages stay in flight), refill the
+    // stage used one step earlier with stage kc + kStages - 1, multiply stage kc.
+    auto step = [&](const char *cur, char *refill, int kc) {
+        wait_dma_barrier<(kStages - 2) * kInstr>();
+        dma(refill, kc + kStages - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
     };
 
-    const int chunks = K / kBK;
-    dma(st0, 0);
-    __syncthreads();
-    int kc = 0;
-    for (; kc + 1 < chunks; kc += 2) {
-        dma(st1, (kc + 1) * kBK);
-        compute(st0);
-        __syncthreads();
-        if (kc + 2 < chunks) dma(st0, (kc + 2) * kBK);
-        compute(st1);
-        __syncthreads();
+    // Rounded up to whole laps of the ring: the extra stages are zeros.
+#pragma unroll
+    for (int i = 0; i + 1 < kStages; ++i) dma(ring[i], i);
+    for (int kc = 0; kc < chunks; kc += kStages) {
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) step(ring[i], ring[(i + kStages - 1) % kStages], kc + i);
     }
-    if (kc < chunks) compute(st0);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): no DMA outlives the loop
 
     // Epilogue: lane holds column n, registers rows 8 (e / 4) + 4 half + e % 4.
 #pragma unroll
@@ -278,14 +343,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
                 const int m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
                 if (m >= M) continue;
                 if constexpr (GATE) {
-                    const __bf16 hv = static_cast<__bf16>(silu(acc0[i][j][e]) * acc1[i][j][e]);
+                    const __bf16 hv = static_cast<__bf16>(silu(acc[i][j][e]) * acc[i][j + 2][e]);
                     out[static_cast<int64_t>(m) * N + n] = __builtin_bit_cast(u16, hv);
                 } else {
                     const int64_t r = rows[m];
                     if (r < 0 || r >= x_rows) continue;
                     u16 *px = out + r * N + n;
                     const float xv = static_cast<float>(__builtin_bit_cast(__bf16, *px));
-                    *px = __builtin_bit_cast(u16, static_cast<__bf16>(xv + acc0[i][j][e]));
+                    *px = __builtin_bit_cast(u16, static_cast<__bf16>(xv + acc[i][j][e]));
                 }
             }
         }
@@ -299,11 +364,11 @@ int launch_sparse_ffn(void *x, int64_t x_rows, int32_t d_model, int32_t d_ff, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const unsigned mt = static_cast<unsigned>((n_sel + kBM - 1) / kBM);
     const int64_t x_bytes = x_rows * d_model * 2, w_bytes = static_cast<int64_t>(d_ff) * d_model * 2;
-    hipLaunchKernelGGL((ffn_gemm_kernel<true>), dim3(static_cast<unsigned>(d_ff / kBN), mt), dim3(kGemmThreads), 0,
+    hipLaunchKernelGGL((ffn_gemm_kernel<true>), dim3(mt, static_cast<unsigned>(d_ff / kBN)), dim3(kGemmThreads), 0,
                        s, static_cast<const u16 *>(x), x_bytes, sel_rows, x_rows, n_sel, d_model,
                        static_cast<const u16 *>(w_gate), static_cast<const u16 *>(w_up), w_bytes, d_ff,
                        static_cast<u16 *>(h));
-    hipLaunchKernelGGL((ffn_gemm_kernel<false>), dim3(static_cast<unsigned>(d_model / kBN), mt), dim3(kGemmThreads),
+    hipLaunchKernelGGL((ffn_gemm_kernel<false>), dim3(mt, static_cast<unsigned>(d_model / kBN)), dim3(kGemmThreads),
                        0, s, static_cast<const u16 *>(h), static_cast<int64_t>(n_sel) * d_ff * 2, sel_rows, x_rows,
                        n_sel, d_ff, static_cast<const u16 *>(w_down), static_cast<const u16 *>(nullptr), w_bytes,
                        d_model, static_cast<u16 *>(x));
