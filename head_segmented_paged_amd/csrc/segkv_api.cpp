@@ -91,10 +91,11 @@ extern "C" int segkv_attn_mass(const segkv_ctx *ctx, const segkv_dev_tables *t, 
     if (!ctx || !t) return fail(SEGKV_ERR_INVALID_ARG, "attn_mass: null argument");
     const segkv_config &cfg = ctx->cfg;
     if (cfg.page_size < 64) return fail(SEGKV_ERR_UNSUPPORTED, "attn_mass: needs page_size >= 64");
-    const segkv::UnitShape shape = segkv::unit_shape(cfg.num_q_heads / cfg.num_kv_heads, cfg.page_size);
-    if (t->unit_rows != shape.rows || t->unit_heads != shape.heads)
-        return fail(SEGKV_ERR_UNSUPPORTED, "attn_mass: needs prefill units of %d rows x %d heads (tables have "
-                    "%d x %d)", shape.rows, shape.heads, t->unit_rows, t->unit_heads);
+    const int G = cfg.num_q_heads / cfg.num_kv_heads;
+    const segkv::UnitShape s4 = segkv::unit_shape(G, segkv::kWaves), s8 = segkv::unit_shape(G, segkv::kWideWaves);
+    if ((t->unit_rows != s4.rows || t->unit_heads != s4.heads) && (t->unit_rows != s8.rows || t->unit_heads != s8.heads))
+        return fail(SEGKV_ERR_UNSUPPORTED, "attn_mass: needs prefill units of %d rows x %d heads or %d x %d (tables "
+                    "have %d x %d)", s4.rows, s4.heads, s8.rows, s8.heads, t->unit_rows, t->unit_heads);
     if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_mass: negative table size");
     if (t->total_q_rows == 0) return SEGKV_OK;
@@ -165,13 +166,16 @@ extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *
     if (o_dtype != SEGKV_DTYPE_F32 && o_dtype != SEGKV_DTYPE_BF16)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: o_dtype must be SEGKV_DTYPE_F32 or SEGKV_DTYPE_BF16");
     const int G = cfg.num_q_heads / cfg.num_kv_heads;
-    const segkv::UnitShape shape = segkv::unit_shape(G, cfg.page_size);
+    const segkv::UnitShape shape = segkv::unit_shape(G, segkv::kWaves);
+    const segkv::UnitShape wide = segkv::unit_shape(G, segkv::kWideWaves);
     const bool decode_ok = segkv::decode_units(G, cfg.page_size, 1) && t->unit_rows == segkv::decode_shape(G).rows &&
                            t->unit_heads == segkv::decode_shape(G).heads;
-    if ((t->unit_rows != shape.rows || t->unit_heads != shape.heads) && !decode_ok)
+    const bool wide_ok = cfg.page_size >= segkv::kKvTile && t->unit_rows == wide.rows && t->unit_heads == wide.heads;
+    if ((t->unit_rows != shape.rows || t->unit_heads != shape.heads) && !decode_ok && !wide_ok)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: tables built for units of %d rows x %d heads, kernels "
-                    "use %d x %d (or %d x %d for decode with pages >= 64)", t->unit_rows, t->unit_heads, shape.rows,
-                    shape.heads, segkv::decode_shape(G).rows, segkv::decode_shape(G).heads);
+                    "use %d x %d (with pages >= 64 also %d x %d, and %d x %d for decode)", t->unit_rows,
+                    t->unit_heads, shape.rows, shape.heads, wide.rows, wide.heads, segkv::decode_shape(G).rows,
+                    segkv::decode_shape(G).heads);
     if (t->num_segments < 0 || t->num_units < 0 || t->num_page_entries < 0 || t->total_q_rows < 0 ||
         t->num_merges < 0 || t->num_parts < 0)
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: negative table size");

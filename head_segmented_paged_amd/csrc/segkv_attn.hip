@@ -507,14 +507,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
 // chunk position keeps the MFMA operand reads free of bank conflicts. The
 // two LDS stages are separate arrays so the compiler can see that reading
 // one never waits for the DMA into the other.
-template <int D>
+template <int D, int NW>
 struct DmaTile {
     static constexpr int kRowBytes = D * 2;                   // one key of K
     static constexpr int kBytes = kBK * kRowBytes;            // K tile
     static constexpr int vBytes = D * kBK * 2;                // V^T tile: D rows of 64 keys
     static constexpr int bytes = kBytes + vBytes;
-    static constexpr int kInstr = kBytes / 1024 / kWaves;     // DMA instructions per wave
-    static constexpr int vInstr = vBytes / 1024 / kWaves;
+    static constexpr int kInstr = kBytes / 1024 / NW;         // DMA instructions per wave
+    static constexpr int vInstr = vBytes / 1024 / NW;
+    static_assert(kInstr >= 1 && vInstr >= 1, "each wave moves at least one KB of a tile");
 };
 // Chunk swizzles: K row r keeps logical chunk c at position c ^ kswz(r); V^T
 // row d keeps key chunk c at position c ^ vswz(d).
@@ -544,16 +545,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const u16 *base, int
 // the matrix cores have independent work during the softmax arithmetic.
 // Buffers: K(j+1) and V(j) are read while K(j+2) and V(j+1) land, two K and two
 // V tiles (the same 64 KB as two whole stages for D = 128).
-template <int D, int HPW, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
+template <int D, int HPW, bool OUT_BF16, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
     int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
     int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse, float *__restrict__ parts,
     int32_t num_parts)
 {
-    using T = DmaTile<D>;
-    constexpr int kRowBlocks = kWaves / HPW;
+    using T = DmaTile<D, NW>;
+    constexpr int kRowBlocks = NW / HPW;
     constexpr int kUnitRows = kWaveRows * kRowBlocks;
     constexpr int kSteps = D / 16;      // MFMA k-steps over the head dim for S^T
     constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_pipe_kernel(
     };
     auto fixup = [&](char *vb, int jt) {
         const int key0 = jt * kBK;
-        for (int e = threadIdx.x; e < D * kBK; e += kThreads) {
+        for (int e = threadIdx.x; e < D * kBK; e += NW * 64) {
             const int d = e / kBK, k = e % kBK, idx = key0 + k;
             if (idx < zero_lo || idx >= zero_hi)
                 *reinterpret_cast<u16 *>(vb + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
@@ -1171,15 +1172,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
 // halves. Each wave adds its 64 column sums to mass[] with float atomics
 // (several heads, row blocks and KV heads reach the same token). Only K is
 // staged; keys before the step (cached tokens) are not visited.
-template <int D, int HPW>
-__global__ __launch_bounds__(kThreads, 2) void attn_mass_kernel(
+template <int D, int HPW, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_mass_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, int64_t num_pages, int log2P,
     const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list, int64_t num_page_entries,
     const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows, int32_t hq, float scale_log2,
     const float *__restrict__ lse, float *__restrict__ mass)
 {
-    using T = DmaTile<D>;
-    constexpr int kRowBlocks = kWaves / HPW;
+    using T = DmaTile<D, NW>;
+    constexpr int kRowBlocks = NW / HPW;
     constexpr int kUnitRows = kWaveRows * kRowBlocks;
     constexpr int kSteps = D / 16;
     __shared__ __attribute__((aligned(1024))) char kst0[T::kBytes];
@@ -1463,8 +1464,15 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
                            t.num_segments, t.total_q_rows, cfg.num_q_heads, t.unit_rows, t.unit_heads, scale_log2,
                            o, lse, parts, t.num_parts);
+    else if (cfg.page_size >= kBK && t.unit_rows * t.unit_heads == kWideWaves * kWaveRows)
+        hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWideWaves>), grid, dim3(kWideWaves * 64), 0,
+                           stream, qh, kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries,
+                           t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts,
+                           t.num_parts);
+    else if constexpr (HPW > kWaves)
+        return;   // eight heads per unit exist only in eight-wave units
     else if (cfg.page_size >= kBK)
-        hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16>), grid, block, 0, stream, qh, kp, vp,
+        hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWaves>), grid, block, 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts, t.num_parts);
     else
@@ -1492,6 +1500,7 @@ void launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void
                   float *lse, float scale_log2, float *parts, hipStream_t stream)
 {
     switch (t.unit_heads) {
+    case 8: launch_dtype<D, 8>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
     case 4: launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
     case 2: launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
     default: launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
@@ -1502,17 +1511,26 @@ template <int D>
 void launch_mass(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, const float *lse,
                  float scale_log2, float *mass, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(t.num_units)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(t.num_units));
     const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
     const int log2P = log2_of(cfg.page_size);
-#define SEGKV_MASS(HPW)                                                                                       \
-    hipLaunchKernelGGL((attn_mass_kernel<D, HPW>), grid, block, 0, stream, qh, kp, cfg.num_pages, log2P,         \
-                       t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments, t.total_q_rows,       \
-                       cfg.num_q_heads, scale_log2, lse, mass)
-    switch (t.unit_heads) {
-    case 4: SEGKV_MASS(4); break;
-    case 2: SEGKV_MASS(2); break;
-    default: SEGKV_MASS(1); break;
+#define SEGKV_MASS(HPW, NW)                                                                                   \
+    hipLaunchKernelGGL((attn_mass_kernel<D, HPW, NW>), grid, dim3(NW * 64), 0, stream, qh, kp, cfg.num_pages,    \
+                       log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,                \
+                       t.total_q_rows, cfg.num_q_heads, scale_log2, lse, mass)
+    if (t.unit_rows * t.unit_heads == kWideWaves * kWaveRows) {
+        switch (t.unit_heads) {
+        case 8: SEGKV_MASS(8, kWideWaves); break;
+        case 4: SEGKV_MASS(4, kWideWaves); break;
+        case 2: SEGKV_MASS(2, kWideWaves); break;
+        default: SEGKV_MASS(1, kWideWaves); break;
+        }
+    } else {
+        switch (t.unit_heads) {
+        case 4: SEGKV_MASS(4, kWaves); break;
+        case 2: SEGKV_MASS(2, kWaves); break;
+        default: SEGKV_MASS(1, kWaves); break;
+        }
     }
 #undef SEGKV_MASS
 }

@@ -17,28 +17,45 @@ void clear_error();
 constexpr int kKvTile = 64;
 // Query rows handled by one wavefront (one 32-wide MFMA column block).
 constexpr int kWaveRows = 32;
-// Wavefronts per attention workgroup.
+// Wavefronts per attention workgroup: four, or for the pipelined kernel
+// (pages of at least one tile) on long contexts eight, whose waves all read the
+// same K/V tiles, so each staged tile feeds twice the MFMAs. Either way a CU
+// holds eight waves, two per SIMD. Eight-wave units start and finish a whole
+// CU at once, which costs more than the shared staging saves when the units'
+// K/V runs are short: they are used from a mean of kWideMinKeys visible keys
+// per query row (and KV head) of the layer.
 constexpr int kWaves = 4;
+constexpr int kWideWaves = 8;
+constexpr int64_t kWideMinKeys = 2048;
+inline int unit_waves(int page_size, bool long_context)
+{
+    return page_size >= kKvTile && long_context ? kWideWaves : kWaves;
+}
 // Work-list cohorts: XCDs of the device (workgroups are dealt to them
-// round-robin by index) and the workgroups one XCD holds at a time (32 CUs,
-// two attention workgroups each).
+// round-robin by index) and the workgroups one XCD holds at a time (32 CUs of
+// eight waves each).
 constexpr int kXcds = 8;
+constexpr int kCuPerXcd = 32;
+inline int cohort(int waves) { return kCuPerXcd * (2 * kWaves) / waves; }
+// The same for decode work lists (single-wave workgroups, dealt like the
+// four-wave ones).
 constexpr int kCohort = 64;
 // Shortest run the automatic split-KV policy cuts a block into (tiles).
 constexpr int kMinRun = 16;
 
 // Shape of one attention work unit for a given GQA group size G: the
-// workgroup's four wavefronts cover `heads` query heads of one group times
-// `rows` query rows, one (head, 32-row block) per wavefront. (The page size is
-// an argument so that kernels with other shapes can be chosen by it.)
+// workgroup's `waves` wavefronts cover `heads` query heads of one group times
+// `rows` query rows, one (head, 32-row block) per wavefront; `heads` is the
+// largest power of two up to the wave count that divides G.
 struct UnitShape {
     int rows;
     int heads;
 };
-inline UnitShape unit_shape(int G, int /*page_size*/)
+inline UnitShape unit_shape(int G, int waves)
 {
-    int heads = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-    return UnitShape{kWaveRows * (kWaves / heads), heads};
+    int heads = 1;
+    while (2 * heads <= waves && G % (2 * heads) == 0) heads *= 2;
+    return UnitShape{kWaveRows * (waves / heads), heads};
 }
 
 // Decode / small-chunk units: every new row of a segment (at most 32 / G)

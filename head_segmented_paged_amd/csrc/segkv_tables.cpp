@@ -60,7 +60,25 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     int max_new = 0;
     for (int32_t b = 0; b < S; ++b) max_new = std::max(max_new, in->new_len[b]);
     const bool decode = segkv::decode_units(G, P, max_new);
-    const segkv::UnitShape shape = decode ? segkv::decode_shape(G) : segkv::unit_shape(G, P);
+    // Mean visible keys per query row and KV head: long contexts get
+    // eight-wave units (a heuristic, summed in double; the inputs are
+    // validated below, and invalid ones are skipped here).
+    double vis_keys = 0.0, vis_rows = 0.0;
+    for (int32_t b = 0; b < S; ++b) {
+        const int64_t c = in->cached_len[b], n = in->new_len[b];
+        if (c < 0 || n < 1 || c > std::numeric_limits<int32_t>::max() || n > std::numeric_limits<int32_t>::max())
+            continue;
+        for (int32_t g = 0; g < hkv; ++g) {
+            const bool global = in->head_class[g] != 0;
+            const int64_t W = global ? 0 : in->window[g];
+            if (!global && W < 1) continue;
+            vis_keys += static_cast<double>(visible_pairs(c, n, W));
+            vis_rows += static_cast<double>(n);
+        }
+    }
+    const int waves =
+        segkv::unit_waves(P, vis_rows > 0.0 && vis_keys >= static_cast<double>(segkv::kWideMinKeys) * vis_rows);
+    const segkv::UnitShape shape = decode ? segkv::decode_shape(G) : segkv::unit_shape(G, waves);
     std::vector<Seg> segs;
     segs.reserve(static_cast<size_t>(S) * hkv);
     int64_t q_rows = 0, pages = 0, units = 0, total_pairs = 0;
@@ -151,7 +169,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
             const int64_t target = static_cast<int64_t>(segkv::kDecodeSlots) * segkv::kDecodeUnitsPerSlot;
             max_run = std::max<int64_t>(segkv::kDecodeMinRun, (total_tiles + target - 1) / target);
         } else {
-            const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::kCohort;
+            const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::cohort(waves);
             if (4 * longest * slots > 3 * total_tiles)
                 max_run = std::max<int64_t>(segkv::kMinRun, (total_tiles + 2 * slots - 1) / (2 * slots));
         }
@@ -248,7 +266,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     // walk the same K/V tiles at about the same time, so one L2 fill serves
     // them all instead of each unit refetching its window from HBM.
     const size_t n_units = list.size();
-    const size_t window = static_cast<size_t>(segkv::kXcds) * segkv::kCohort;
+    const size_t window = static_cast<size_t>(segkv::kXcds) * (decode ? segkv::kCohort : segkv::cohort(waves));
     std::vector<Unit> dealt(n_units);
     for (size_t base = 0; base < n_units; base += window) {
         const size_t n = std::min(window, n_units - base);

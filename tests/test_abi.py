@@ -150,6 +150,8 @@ def test_split_tables_need_a_workspace():
     assert rc == S.SEGKV_ERR_INVALID_ARG and "merge" in H.segkv_last_error()
     # pages shorter than a tile: the builder never splits, hand-made split tables are refused
     ctx16 = _ctx(4, 1, 128, 16, 64)
+    dt.unit_rows, dt.unit_heads = 32, 4          # the short-page kernel's unit: four waves, G = 4
+    dt.merge = 9
     rc = S._lib.segkv_attn_prefill(ctx16.handle, ctypes.byref(dt), 4, 5, S.SEGKV_DTYPE_F32, None, 0.0, 8,
                                    host["workspace_bytes"], None)
     assert rc == S.SEGKV_ERR_UNSUPPORTED

@@ -130,6 +130,32 @@ def test_split_kv_all_rows(case):
     assert torch.equal(ob, o.to(torch.bfloat16))
 
 
+WIDE = [
+    # long contexts (mean visible keys per row >= 2048): eight-wave units of 256
+    # (row, head) pairs; (hq, hkv, d, page, window, classes, seqs, run: 0 automatic)
+    (8, 1, 128, 64, 0, (1,), ((3000, 300),), 0),
+    (8, 1, 128, 64, 0, (1,), ((3000, 300),), 4),
+    (4, 2, 64, 128, 3000, (1, 0), ((2500, 200), (4000, 77)), 0),
+    (2, 2, 128, 256, 0, (1, 1), ((2100, 513),), 3),
+    (16, 2, 128, 64, 2500, (0, 1), ((5000, 100), (2200, 33)), 0),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_run{c[7]}")
+def test_wide_units_all_rows(case):
+    """Eight-wave units (one K/V stream for 256 pairs), with and without split
+    runs, G from 1 to 8: every row against the oracle; bf16 output is RNE of
+    fp32."""
+    hq, hkv, d, page, window, classes, seqs, run = case
+    w = adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * 7 + d + run)
+    o, lse, gl = run_case(w, max_unit_tiles=run if run else -1)
+    assert gl.host["unit_rows"] * gl.host["unit_heads"] == 256
+    assert (gl.host["num_parts"] > 0) == (run > 0)
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+
+
 DECODE = [
     # (hq, hkv, d, page, window, classes, seqs, longest run in tiles: 0 automatic)
     (8, 2, 128, 64, 100, (0, 1), ((300, 1), (37, 5), (1000, 8), (5, 3)), 0),

@@ -40,10 +40,23 @@ def _compare(w, r, layer, ctx):
     return lib
 
 
-WINDOW = 512   # 8 XCDs x 64 workgroups: the cohort window of the work list
+def _waves(w, lib):
+    """Wavefronts per prefill workgroup: eight for pages of at least one tile
+    when the layer's mean visible keys per query row and KV head reach 2048
+    (sum of visible pairs over its segments, from the oracle-checked
+    total_pairs, against 2048 x rows), four otherwise."""
+    G = w.hq // w.hkv
+    long_context = lib["total_pairs"] >= 2048 * G * w.hkv * lib["total_q_rows"]
+    return 8 if w.page >= 64 and long_context else 4
 
 
-def _check_order(work):
+def _window(waves, decode):
+    """Cohort window of the work list: 8 XCDs x the workgroups one XCD holds
+    (32 CUs x 8 waves / waves per workgroup; decode lists use 64)."""
+    return 8 * (64 if decode else 32 * 8 // waves)
+
+
+def _check_order(work, WINDOW):
     """Longest first between windows; inside a window, each XCD's share
     (positions x, x+8, ...) in (segment, row, head) order."""
     tiles = work[:, 3]
@@ -70,10 +83,11 @@ def _check_work(lib, w):
     work = lib["work"]
     rows, heads = lib["unit_rows"], lib["unit_heads"]
     decode = w.page >= 64 and G <= 32 and int(lib["n_q"].max()) <= 32 // G
-    prefill_heads = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
-    assert (heads, rows) == ((G, 32 // G) if decode else (prefill_heads, 128 // prefill_heads))
+    waves = _waves(w, lib)
+    prefill_heads = max(h for h in (1, 2, 4, 8) if h <= waves and G % h == 0)
+    assert (heads, rows) == ((G, 32 // G) if decode else (prefill_heads, 32 * waves // prefill_heads))
     assert (work[:, 6:] == 0).all()
-    _check_order(work)
+    _check_order(work, _window(waves, decode))
     # blocks: every (segment, head, row) in exactly one block; a block's units
     # cut its natural run of tiles into consecutive pieces
     blocks = {}
@@ -128,7 +142,7 @@ def test_stack_all_layers():
         lib = _compare(w, r, layer, ctx)
         if layer in (0, 8, 63):
             work = lib["work"]
-            _check_order(work)
+            _check_order(work, _window(_waves(w, lib), False))
             assert len(work) == 8 * (131072 // lib["unit_rows"])
 
 
