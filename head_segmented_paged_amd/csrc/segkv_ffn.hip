@@ -175,8 +175,12 @@ template <int N>
 __device__ __forceinline__ void wait_dma_barrier()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
+    // The empty asm statements are compiler memory barriers: no load or store
+    // of shared memory moves across the wait and the barrier.
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
