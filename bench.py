@@ -185,7 +185,7 @@ def algorithmic_bytes(w, r, o_bytes=2):
     return qo + kv / w.layers
 
 
-def cpu_baseline(res, target_s=12.0):
+def cpu_baseline(res, target_s=18.0):
     """The fp64 oracle, as it stands, on a bounded sample of one layer's queries."""
     from oracle import paged as opaged
     from oracle import tables as otables
