@@ -23,13 +23,15 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def run_mass(w, max_unit_tiles=0):
+def run_mass(w, max_unit_tiles=0, unit_pairs=None):
     r = realize(w)
     say(f"[case] mass {w.name} hq {w.hq} hkv {w.hkv} D {w.d} P {w.page} "
         f"seqs {list(zip(r.cached_len.tolist(), r.new_len.tolist()))[:4]} run {max_unit_tiles}")
     t = layer_tensors(w, r, 0, device="cuda")
     gl = GpuLayer(w, r, 0, t, max_unit_tiles=max_unit_tiles)
     o, lse = gl.run()
+    if unit_pairs is not None:
+        assert gl.host["unit_rows"] * gl.host["unit_heads"] == unit_pairs
     mass = torch.empty(int(r.new_len.sum()), dtype=torch.float32, device="cuda")
     H.segkv_attn_mass(gl.ctx, gl.dev, t["q"], lse, mass)
     torch.cuda.synchronize()
@@ -62,6 +64,21 @@ def test_mass_all_tokens(case):
     hq, hkv, d, page, window, classes, seqs, run = case
     run_mass(adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq * d + page),
              max_unit_tiles=run)
+
+
+MASS_WIDE = [
+    # long cached prefixes (mean visible keys per row >= 2048): eight-wave units
+    (8, 1, 128, 64, 0, (1,), ((3000, 300),), 0),
+    (4, 2, 64, 128, 3000, (1, 0), ((2500, 200), (4000, 77)), 4),
+    (2, 2, 128, 256, 0, (1, 1), ((2100, 513),), 0),
+]
+
+
+@pytest.mark.parametrize("case", MASS_WIDE, ids=lambda c: f"hq{c[0]}_kv{c[1]}_d{c[2]}_p{c[3]}_run{c[7]}")
+def test_mass_wide_units(case):
+    hq, hkv, d, page, window, classes, seqs, run = case
+    run_mass(adhoc(hq=hq, hkv=hkv, d=d, page=page, window=window, classes=classes, seqs=seqs, seed=hq + d + page),
+             max_unit_tiles=run, unit_pairs=256)
 
 
 def test_mass_8k():
