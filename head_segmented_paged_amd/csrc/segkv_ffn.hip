@@ -146,14 +146,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kGemmThreads = 512;                 // eight waves, two per SIMD
 constexpr int kBM = 256;                    // A rows (chosen tokens) per tile
 constexpr int kBN = 128;                    // output columns per tile
-constexpr int kBK = 32;                     // K per stage
-constexpr int kRowBytes = kBK * 2;          // 64 B per tile row
-constexpr int kATileBytes = kBM * kRowBytes;   // 16 KB
 
-// Row r of a tile keeps its 16-byte chunk c at position c ^ gswz(r): sixteen
-// lanes reading one chunk of sixteen consecutive rows hit sixteen distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
+// Row r of a tile of BK-wide rows keeps its 16-byte chunk c at position
+// c ^ gswz<BK>(r): sixteen lanes reading one chunk of sixteen consecutive rows
+// hit sixteen distinct 16-byte bank groups (64-byte rows: four rows per
+// 256-byte bank line, four chunk positions; 128-byte rows: two and eight).
+template <int BK>
+__device__ __forceinline__ int gswz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 __device__ __forceinline__ void gdma16(__amdgpu_buffer_rsrc_t rsrc, char *lds, unsigned voffset, unsigned soffset)
 {
@@ -199,18 +198,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
     int32_t K, const u16 *__restrict__ b0, const u16 *__restrict__ b1, int64_t b_bytes, int32_t N,
     u16 *__restrict__ out)
 {
+    // K per stage: 32 for GATE (whose stages carry twice the MFMAs), 64 for
+    // the down projection, so both run about 1024 MFMA cycles between barriers.
+    constexpr int kBK = GATE ? 32 : 64;
+    constexpr int kRowBytes = kBK * 2;
+    constexpr int kATileBytes = kBM * kRowBytes;
     constexpr int kBRows = GATE ? 2 * kBN : kBN;           // B tile rows: gate rows then up rows, or down rows
     constexpr int kBTileBytes = kBRows * kRowBytes;
-    constexpr int kStage = kATileBytes + kBTileBytes;      // 32 KB or 24 KB
+    constexpr int kStage = kATileBytes + kBTileBytes;      // 32 KB or 48 KB
     constexpr int kAInstr = kATileBytes / 1024 / 8;        // DMA instructions per wave and stage
     constexpr int kBInstr = kBTileBytes / 1024 / 8;
     constexpr int kInstr = kAInstr + kBInstr;
     constexpr int kBCols = GATE ? 4 : 2;                   // 32-column B blocks per wave (gate 0, 1; up 2, 3)
-    // LDS ring of kStages stages (128 KB and 96 KB), indexed by constants
+    // LDS ring of kStages stages (128 KB and 144 KB), indexed by constants
     // only, so the compiler sees that a DMA into one stage does not alias the
-    // LDS reads of another and adds no wait for it. Five- and six-stage rings
+    // LDS reads of another and adds no wait for it. Deeper rings for GATE
     // measured no faster.
-    constexpr int kStages = 4;
+    constexpr int kStages = GATE ? 4 : 3;
     __shared__ __attribute__((aligned(1024))) char ring[kStages][kStage];
 
     const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kAInstr; ++i) {
         const int p = (wave * kAInstr + i) * 1024 + lane * 16;
-        const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz(r);
+        const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz<kBK>(r);
         const int m = m0 + r;
         int64_t arow = -1;
         if (m < M) arow = GATE ? rows[m] : m;
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kBInstr; ++i) {
         const int p = (wave * kBInstr + i) * 1024 + lane * 16;
-        const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz(r);
+        const int r = p / kRowBytes, c = ((p % kRowBytes) / 16) ^ gswz<kBK>(r);
         const int wrow = n0 + (r % kBN);
         boff[i] = static_cast<unsigned>(static_cast<int64_t>(wrow) * K * 2 + c * 16);
     }
@@ -266,13 +270,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
     for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + 32 * i + col;
         arow_lds[i] = static_cast<unsigned>(r * kRowBytes);
-        aswz[i] = gswz(r);
+        aswz[i] = gswz<kBK>(r);
     }
 #pragma unroll
     for (int j = 0; j < kBCols; ++j) {
         const int r = (j >> 1) * kBN + wn * 64 + 32 * (j & 1) + col;
         brow_lds[j] = static_cast<unsigned>(kATileBytes + r * kRowBytes);
-        bswz[j] = gswz(r);
+        bswz[j] = gswz<kBK>(r);
     }
 
     f32x16 acc[2][kBCols];
@@ -299,24 +303,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
             for (int j = 0; j < kBCols; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a[i], op.b[j], acc[i][j], 0, 0, 0);
     };
-    // The second k-step's operands are read while the first k-step's MFMAs
-    // run: the scheduling groups put one LDS read after each of the first
-    // MFMAs (the compiler would otherwise read each step's operands right
+    // Each k-step's operands are read while the previous k-step's MFMAs run:
+    // the scheduling groups put one LDS read after each of the first MFMAs of
+    // a step (the compiler would otherwise read each step's operands right
     // before its MFMAs and leave the matrix core idle for the LDS latency).
+    constexpr int kKSteps = kBK / 16;
     auto compute = [&](const char *stage) {
         Ops x, y;
         load_ops(x, stage, 0);
-        load_ops(y, stage, 1);
-        mfmas(x);
-        mfmas(y);
+#pragma unroll
+        for (int s = 0; s < kKSteps; s += 2) {
+            load_ops(y, stage, s + 1);
+            mfmas(x);
+            if (s + 2 < kKSteps) load_ops(x, stage, s + 2);
+            mfmas(y);
+        }
         constexpr int kReads = 2 + kBCols, kMfma = 2 * kBCols;
         __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
-        for (int r = 0; r < kReads; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int st = 0; st + 1 < kKSteps; ++st) {
+#pragma unroll
+            for (int r = 0; r < kReads; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfma - kReads, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
     };
     // Stage kc: wait for its DMA (the newer stages stay in flight), refill the
     // stage used one step earlier with stage kc + kStages - 1, multiply stage kc.
