@@ -191,16 +191,17 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __builtin_am
 // up projection of it), eight waves of 64 x 64 each, two per SIMD. The tile
 // size sets how many bytes each MFMA needs from L2: 128 flops per byte staged
 // into LDS here, against 64-85 for 128 x 128 tiles. Operands stream through an
-// LDS ring of 32-wide K slices, all but one in flight while one is multiplied.
+// LDS ring of 64-wide K slices, all but one in flight while one is multiplied.
 template <bool GATE>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
     const u16 *__restrict__ a, int64_t a_bytes, const int32_t *__restrict__ rows, int64_t x_rows, int32_t M,
     int32_t K, const u16 *__restrict__ b0, const u16 *__restrict__ b1, int64_t b_bytes, int32_t N,
     u16 *__restrict__ out)
 {
-    // K per stage: 32 for GATE (whose stages carry twice the MFMAs), 64 for
-    // the down projection, so both run about 1024 MFMA cycles between barriers.
-    constexpr int kBK = GATE ? 32 : 64;
+    // K per stage: 64 (each stage's barrier is amortised over 2048 MFMA cycles
+    // per SIMD for GATE, 1024 for the down projection; 32-wide slices in
+    // deeper rings measured 4-7 % slower).
+    constexpr int kBK = 64;
     constexpr int kRowBytes = kBK * 2;
     constexpr int kATileBytes = kBM * kRowBytes;
     constexpr int kBRows = GATE ? 2 * kBN : kBN;           // B tile rows: gate rows then up rows, or down rows
@@ -210,11 +211,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_gemm_kernel(
     constexpr int kBInstr = kBTileBytes / 1024 / 8;
     constexpr int kInstr = kAInstr + kBInstr;
     constexpr int kBCols = GATE ? 4 : 2;                   // 32-column B blocks per wave (gate 0, 1; up 2, 3)
-    // LDS ring of kStages stages (128 KB and 144 KB), indexed by constants
-    // only, so the compiler sees that a DMA into one stage does not alias the
-    // LDS reads of another and adds no wait for it. Deeper rings for GATE
-    // measured no faster.
-    constexpr int kStages = GATE ? 4 : 3;
+    // LDS ring of kStages stages (2 x 64 KB and 3 x 48 KB), indexed by
+    // constants only, so the compiler sees that a DMA into one stage does not
+    // alias the LDS reads of another and adds no wait for it.
+    constexpr int kStages = GATE ? 2 : 3;
     __shared__ __attribute__((aligned(1024))) char ring[kStages][kStage];
 
     const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
