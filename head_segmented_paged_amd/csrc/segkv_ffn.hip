@@ -134,8 +134,10 @@ namespace {
 // for the chosen rows r_m; every other row of x is left as it is (the
 // residual identity path). Both products are bf16 MFMA GEMMs with K
 // contiguous in both operands (weights stored [out][in]); the chosen rows are
-// gathered straight from x by the DMA. Tile 128 x 128, K chunks of 64 in a
-// two-stage LDS ring, four waves of 64 x 64 (2 x 2 blocks of 32 x 32).
+// gathered straight from x by the DMA. Tile 256 x 128 (for the first product
+// the gate and the up projection of it), K slices of 64 in an LDS ring, eight
+// waves of 64 x 64 (2 x 2 blocks of 32 x 32; for the first product also the
+// up projection's 2 x 2).
 // ---------------------------------------------------------------------------
 
 typedef unsigned short u16;
