@@ -893,8 +893,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
 // segment's few new rows for all G query heads of its KV head: column c of
 // the MFMAs is the (row c / G, head c % G) pair, so the 32 columns carry up to
 // 32 / G rows. The step is bound by HBM bandwidth. Each workgroup is a single
-// wavefront that streams its unit's 32-key blocks straight from the pages into
-// its MFMA operand registers, loading the next block while it computes the
+// wavefront that streams its unit's 64-key tiles straight from the pages into
+// its MFMA operand registers, loading the next tile while it computes the
 // current one; eight such workgroups share a CU, so one wave's start (reading
 // its unit's descriptors, Q and page ids) and finish (writing its result)
 // overlap the other waves' streaming, and no wave waits for another.
