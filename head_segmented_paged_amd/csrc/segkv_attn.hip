@@ -1340,95 +1340,79 @@ __global__ void fill_zero_kernel(float *__restrict__ x, int64_t n)
 // entry, each for a quarter of the head dim. The runs' partial results
 // combine exactly as blocks of one online softmax:
 // O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with M the largest m_r.
-// First the workgroup reduces (M, L) of every valid (row, head) pair, several
-// lanes per pair each over a stride of the runs; then each lane owns four
-// consecutive dims of one pair and sums the weighted O_r of a stride of the
-// runs (few pairs: several lanes per item, added up in LDS), so a wave reads
-// whole rows of the partial results and the loads of many runs overlap.
+// Every lane owns four consecutive dims of one valid (row, head) pair and
+// folds a stride of the runs into a running (M, L, O) in one pass (several
+// lanes per item when the block has few pairs, combined in LDS the same way),
+// so a wave reads whole rows of the partials, the loads of many runs overlap,
+// and the entry itself carries the output rows (no segment lookup).
 constexpr int kMergeDSplit = 4;
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
-    const int32_t *__restrict__ merge, const int32_t *__restrict__ seg_desc, int32_t num_segments,
-    const float *__restrict__ parts, int32_t num_parts, int32_t unit_rows, int32_t unit_heads,
-    int32_t total_q_rows, int32_t hq, void *__restrict__ o, float *__restrict__ lse)
+    const int32_t *__restrict__ merge, const float *__restrict__ parts, int32_t num_parts, int32_t unit_rows,
+    int32_t unit_heads, int32_t total_q_rows, int32_t hq, void *__restrict__ o, float *__restrict__ lse)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    __shared__ float red_m[kThreads], red_l[kThreads], fin_m[kThreads], fin_l[kThreads];
+    __shared__ float red_m[kThreads], red_l[kThreads];
     __shared__ f32x4 red_o[kThreads];
     const int32_t *e = merge + static_cast<int64_t>(blockIdx.x) * SEGKV_MERGE_FIELDS;
-    const int seg = e[SEGKV_MERGE_SEGMENT], row0 = e[SEGKV_MERGE_ROW0], head0 = e[SEGKV_MERGE_HEAD0];
-    const int part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
-    if (seg < 0 || seg >= num_segments || part0 < 0 || nparts < 1 || part0 > num_parts - nparts) return;
-    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
-    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q];
+    const int head0 = e[SEGKV_MERGE_HEAD0], part0 = e[SEGKV_MERGE_PART0], nparts = e[SEGKV_MERGE_NPARTS];
+    const int out_row0 = e[SEGKV_MERGE_OUT_ROW0], rows_ok = e[SEGKV_MERGE_ROWS];
     const int pairs = unit_rows * unit_heads;
-    const int rows_ok = min(unit_rows, n_q - row0), heads_ok = min(unit_heads, hq - head0);
+    const int heads_ok = min(unit_heads, hq - head0);
+    if (part0 < 0 || nparts < 1 || part0 > num_parts - nparts || rows_ok < 1 || rows_ok > unit_rows ||
+        out_row0 < 0 || out_row0 > total_q_rows - rows_ok || head0 < 0 || heads_ok < 1 || pairs > kThreads)
+        return;
     const int nv = rows_ok * heads_ok;   // valid pairs, vr = head-major over rows_ok
-    if (rows_ok < 1 || heads_ok < 1 || pairs > kThreads) return;
     const int64_t kSlot = static_cast<int64_t>(pairs) * (D + 2);   // floats per partial result
     const float *base = parts + static_cast<int64_t>(part0) * kSlot;
-    auto slot_pair = [&](int vr) { return (vr / rows_ok) * unit_rows + vr % rows_ok; };
-
-    // (M, L) per valid pair: kThreads / nv lanes per pair, combined in LDS.
-    const int per = kThreads / nv, i = threadIdx.x;
-    {
-        float M = kNegBig, L = 0.f;
-        if (i < per * nv) {
-            const int r = slot_pair(i % nv);
-            for (int p = i / nv; p < nparts; p += per) {
-                const float mp = base[p * kSlot + pairs * D + r], lp = base[p * kSlot + pairs * (D + 1) + r];
-                const float mn = fmaxf(M, mp);
-                L = L * __builtin_amdgcn_exp2f(M - mn) + lp * __builtin_amdgcn_exp2f(mp - mn);
-                M = mn;
-            }
-        }
-        red_m[i] = M;
-        red_l[i] = L;
-    }
-    __syncthreads();
-    if (i < nv) {
-        float M = kNegBig, L = 0.f;
-        for (int g = 0; g < per; ++g) M = fmaxf(M, red_m[g * nv + i]);
-        for (int g = 0; g < per; ++g) L += red_l[g * nv + i] * __builtin_amdgcn_exp2f(red_m[g * nv + i] - M);
-        fin_m[i] = M;
-        fin_l[i] = L;
-    }
-    __syncthreads();
 
     // This workgroup's dims: chunks [c0, c0 + kChunks) of four.
     constexpr int kChunks = D / 4 / kMergeDSplit;
     const int c0 = static_cast<int>(blockIdx.y) * kChunks;
-    const int items = nv * kChunks;
+    const int items = nv * kChunks, i = threadIdx.x;
     const int groups = items < kThreads ? kThreads / items : 1;   // lanes per item, each over a stride of runs
     const int grp = i / (items < kThreads ? items : kThreads);
     for (int item0 = 0; item0 < items; item0 += kThreads) {
         const int item = item0 + (groups > 1 ? i % items : i);
         const bool mine = item < items && grp < groups;
         const int vr = mine ? item / kChunks : 0, ch = c0 + (mine ? item % kChunks : 0);
-        const int r = slot_pair(vr);
+        const int r = (vr / rows_ok) * unit_rows + vr % rows_ok;   // the pair's slot in a partial result
+        float M = kNegBig, L = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (mine) {
-            const float M = fin_m[vr];
-#pragma unroll 8
+#pragma unroll 4
             for (int p = grp; p < nparts; p += groups) {
                 const float *slot = base + p * kSlot;
-                const float w = __builtin_amdgcn_exp2f(slot[pairs * D + r] - M);
-                acc += w * *reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + 4 * ch);
+                const float mp = slot[pairs * D + r], lp = slot[pairs * (D + 1) + r];
+                const f32x4 op = *reinterpret_cast<const f32x4 *>(slot + static_cast<int64_t>(r) * D + 4 * ch);
+                const float mn = fmaxf(M, mp);
+                const float a = __builtin_amdgcn_exp2f(M - mn), w = __builtin_amdgcn_exp2f(mp - mn);
+                acc = acc * a + op * w;
+                L = L * a + lp * w;
+                M = mn;
             }
         }
         if (groups > 1) {
+            red_m[i] = M;
+            red_l[i] = L;
             red_o[i] = acc;
             __syncthreads();
-            if (grp == 0)
-                for (int g = 1; g < groups; ++g) acc += red_o[g * items + i];
+            if (grp == 0) {
+                for (int g = 1; g < groups; ++g) M = fmaxf(M, red_m[g * items + i]);
+                L = 0.f;
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int g = 0; g < groups; ++g) {
+                    const float w = __builtin_amdgcn_exp2f(red_m[g * items + i] - M);
+                    L += red_l[g * items + i] * w;
+                    acc += red_o[g * items + i] * w;
+                }
+            }
         }
         if (!mine || grp != 0) continue;
-        const int head = head0 + vr / rows_ok, t = row0 + vr % rows_ok;
-        const int64_t row = static_cast<int64_t>(q_row0) + t;
-        if (row >= total_q_rows) continue;
-        const float M = fin_m[vr], l = fin_l[vr];
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const int head = head0 + vr / rows_ok;
+        const int64_t row = static_cast<int64_t>(out_row0) + vr % rows_ok;
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
         const f32x4 v = acc * inv;
         const int64_t obase = (row * hq + head) * D + 4 * ch;
         if constexpr (OUT_BF16) {
@@ -1440,7 +1424,7 @@ __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
             *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase) = v;
         }
         if (lse && ch == 0)
-            lse[static_cast<int64_t>(head) * total_q_rows + row] = (M + __log2f(l)) * 0.69314718055994530942f;
+            lse[static_cast<int64_t>(head) * total_q_rows + row] = (M + __log2f(L)) * 0.69314718055994530942f;
     }
 }
 
@@ -1481,8 +1465,8 @@ void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, v
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse);
     if (t.num_merges > 0)
         hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges), kMergeDSplit),
-                           block, 0, stream, t.merge, t.seg_desc, t.num_segments, parts, t.num_parts, t.unit_rows,
-                           t.unit_heads, t.total_q_rows, cfg.num_q_heads, o, lse);
+                           block, 0, stream, t.merge, parts, t.num_parts, t.unit_rows, t.unit_heads, t.total_q_rows,
+                           cfg.num_q_heads, o, lse);
 }
 
 template <int D, int HPW>

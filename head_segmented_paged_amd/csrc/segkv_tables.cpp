@@ -185,8 +185,10 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
                 continue;
             }
             const int64_t nr = (u.tiles + max_run - 1) / max_run;
+            const Seg &sg = segs[static_cast<size_t>(u.seg)];
             const int32_t merge[SEGKV_MERGE_FIELDS] = {u.seg, u.row0, u.head0, static_cast<int32_t>(n_parts),
-                                                       static_cast<int32_t>(nr), 0, 0, 0};
+                                                       static_cast<int32_t>(nr), sg.q_row0 + u.row0,
+                                                       std::min(shape.rows, sg.n_q - u.row0), 0};
             merges.insert(merges.end(), merge, merge + SEGKV_MERGE_FIELDS);
             for (int64_t r = 0; r < nr; ++r) {   // runs of near-equal length
                 const int64_t a = u.tiles * r / nr, b = u.tiles * (r + 1) / nr;

@@ -106,7 +106,9 @@ enum {
     SEGKV_MERGE_HEAD0 = 2,
     SEGKV_MERGE_PART0 = 3,
     SEGKV_MERGE_NPARTS = 4,
-    SEGKV_MERGE_FIELDS = 8  /* fields 5 .. 7 are zero */
+    SEGKV_MERGE_OUT_ROW0 = 5,   /* first output row of the block: the segment's q_row0 + row0 */
+    SEGKV_MERGE_ROWS = 6,       /* rows of the block that exist: min(unit_rows, n_b - row0) */
+    SEGKV_MERGE_FIELDS = 8      /* field 7 is zero */
 };
 
 /* Workspace bytes per partial result: the unit's unit_rows * unit_heads

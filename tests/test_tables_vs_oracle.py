@@ -103,7 +103,9 @@ def _check_work(lib, w):
         assert (cnt == 1).all()
     merges = {(int(m[0]), int(m[1]), int(m[2])): m for m in lib["merge"]}
     assert len(merges) == lib["num_merges"] == len(lib["merge"])
-    assert (lib["merge"][:, 5:] == 0).all() if len(lib["merge"]) else True
+    for m in lib["merge"]:   # output rows of the block, straight from its segment
+        seg, r0 = int(m[0]), int(m[1])
+        assert m[5] == lib["q_row0"][seg] + r0 and m[6] == min(rows, lib["n_q"][seg] - r0) and m[7] == 0
     seen_parts = []
     for key, units in blocks.items():
         seg, r0, h0 = key
