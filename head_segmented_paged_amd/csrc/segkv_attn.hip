@@ -959,17 +959,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
     const int all_lo = max(window ? last_pos - window + 1 : 0, run_lo);
     const int all_hi = min(first_pos, run_hi);
 
-    // Q^T, the B operand (lane column = pair), sits in LDS for the loop.
-    for (int i = lane; i < kWaveRows * (D / 8); i += kDecThreads) {
-        const int qc = i / (D / 8), qd = 8 * (i % (D / 8));
-        const int qr = qc / unit_heads, qh = qc % unit_heads;
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qc < unit_rows * unit_heads && row0 + qr < n_q && head0 + qh < hq) {
-            const int64_t qrow = static_cast<int64_t>(q_row0) + row0 + qr;
-            if (qrow < total_q_rows) raw = *reinterpret_cast<const u32x4 *>(q + (qrow * hq + head0 + qh) * D + qd);
-        }
-        *reinterpret_cast<u32x4 *>(qlds + qc * kQLd + qd) = raw;
-    }
     const u16 *qcol = qlds + col * kQLd + 8 * half;
     f32x16 oacc[kDBlocks];
 #pragma unroll
@@ -1000,8 +989,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
         if (tile < pass_end) page = __builtin_amdgcn_readfirstlane(ids[tile / tiles_per_page - id0]);
         return page;
     };
-    auto fetch_k = [&](int tile) {
-        const int page = page_of(tile);
+    auto fetch_k_pg = [&](int page, int tile) {
         const int pg = max(page, 0);
         const __amdgpu_buffer_rsrc_t rk =
             page_rsrc(kpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
@@ -1013,8 +1001,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
                 kreg[g][s] = __builtin_bit_cast(
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 32 * g * D * 2 + 32 * s, 0, 0));
     };
-    auto fetch_v = [&](int tile) {
-        const int page = page_of(tile);
+    auto fetch_v_pg = [&](int page, int tile) {
         const int pg = max(page, 0);
         const __amdgpu_buffer_rsrc_t rv =
             page_rsrc(vpool + ((static_cast<int64_t>(pg) * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
@@ -1026,6 +1013,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
                 vreg[t][db] = __builtin_bit_cast(
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off + 64 * db * P + 32 * t, 0, 0));
     };
+
+    auto fetch_k = [&](int tile) { fetch_k_pg(page_of(tile), tile); };
+    auto fetch_v = [&](int tile) { fetch_v_pg(page_of(tile), tile); };
 
     // One tile: S^T, then the next tile's K is requested; the softmax; P V,
     // then the next tile's V is requested.
@@ -1102,20 +1092,67 @@ __global__ __launch_bounds__(kDecThreads, 2) void attn_decode_kernel(
 
     // Passes over the pages of each kIdCap-page stretch of the segment, one
     // tile per step (the tile past a pass is requested as an empty range).
-    for (int pass_beg = tile_beg; pass_beg < tile_end; pass_beg = pass_end) {
-        pass_end = min(tile_end, (pass_beg / tiles_per_pass + 1) * tiles_per_pass);
-        id0 = pass_beg / tiles_per_page;
+    // The first pass takes its first tile's page by a scalar load, so that
+    // tile's K and V requests go out right after Q's and beside the ids'
+    // instead of after them.
+    // Q^T, the B operand (lane column = pair), sits in LDS for the loop. All
+    // of a lane's chunks are requested before any is written (one round trip,
+    // not one per chunk).
+    // Buffer loads over the unit's rows of Q: a lane with nothing to load
+    // gets an offset past the range and reads zeros, so no load sits behind a
+    // branch (which would make the compiler wait for each before the next).
+    constexpr int kQChunks = kWaveRows * (D / 8) / kDecThreads;
+    const int64_t qrow0 = static_cast<int64_t>(q_row0) + row0;
+    const int q_rows = static_cast<int>(max<int64_t>(0, min<int64_t>(unit_end - row0, total_q_rows - qrow0)));
+    const __amdgpu_buffer_rsrc_t rq = page_rsrc(q + qrow0 * hq * D, q_rows * hq * D * 2);
+    u32x4 qraw[kQChunks];
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) {
+        const int i = lane + c * kDecThreads;
+        const int qc = i / (D / 8), qd = 8 * (i % (D / 8));
+        const int qr = qc / unit_heads, qh = qc % unit_heads;
+        const bool ok = qc < unit_rows * unit_heads && qr < q_rows && head0 + qh < hq;
+        const unsigned off = ok ? static_cast<unsigned>(((qr * hq + head0 + qh) * D + qd) * 2) : 0x80000000u;
+        qraw[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) {
+        const int i = lane + c * kDecThreads;
+        *reinterpret_cast<u32x4 *>(qlds + (i / (D / 8)) * kQLd + 8 * (i % (D / 8))) = qraw[c];
+    }
+    int pass_beg = tile_beg;
+    pass_end = min(tile_end, (pass_beg / tiles_per_pass + 1) * tiles_per_pass);
+    id0 = pass_beg / tiles_per_page;
+    {
+        int pg0 = -1;
+        if (tile_beg < tile_end && id0 < n_pages) {
+            const int v = pages[id0];
+            pg0 = (v >= 0 && v < num_pages) ? v : -1;
+        }
+        fetch_k_pg(pg0, pass_beg);
+        fetch_v_pg(pg0, pass_beg);
+    }
+    auto stage_ids = [&]() {
         const int n_ids = (pass_end - 1) / tiles_per_page - id0 + 1;
         for (int i = lane; i < n_ids; i += kDecThreads) {
             int page = -1;
             if (id0 + i < n_pages) page = pages[id0 + i];
             ids[i] = (page >= 0 && page < num_pages) ? page : -1;
         }
-        __syncthreads();   // the ids (and on the first pass Q^T) are visible to every lane
+    };
+    stage_ids();
+    __syncthreads();   // Q^T and the ids are visible to every lane
+    for (int tile = pass_beg; tile < pass_end; ++tile) compute(tile);
+    __syncthreads();   // every lane is done with the ids before a next pass rewrites them
+    for (pass_beg = pass_end; pass_beg < tile_end; pass_beg = pass_end) {
+        pass_end = min(tile_end, (pass_beg / tiles_per_pass + 1) * tiles_per_pass);
+        id0 = pass_beg / tiles_per_page;
+        stage_ids();
+        __syncthreads();
         fetch_k(pass_beg);
         fetch_v(pass_beg);
         for (int tile = pass_beg; tile < pass_end; ++tile) compute(tile);
-        __syncthreads();   // every lane is done with the ids before the next pass rewrites them
+        __syncthreads();
     }
 
     // Results straight from the O^T registers: lane (col, half) holds dims
