@@ -420,6 +420,10 @@ def main():
         "roofline": roof,
         "algorithmic_bytes_per_launch": algo_bytes,
         "globals_per_layer": globals_per_layer,
+        # mean attention time of the layers with 0, 1, 2, ... global KV heads
+        "ms_per_layer_by_globals": {
+            str(g): float(attn.mean(axis=0)[np.asarray(globals_per_layer) == g].mean())
+            for g in sorted(set(globals_per_layer))},
     }
     if not args.no_secondary and w.name == "stack64_l131072":
         del res
