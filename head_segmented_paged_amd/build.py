@@ -50,6 +50,8 @@ def _run(cmd):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
+    # the two-block prefill kernel's tile bodies are generated (no-op when current)
+    _run([sys.executable, os.path.join(CSRC, "gen_tile_asm.py")])
     jobs = []
     objs = []
     for src in HIP_SOURCES:

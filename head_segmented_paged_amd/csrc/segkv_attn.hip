@@ -108,7 +108,6 @@ __device__ __forceinline__ float sum_halves(float x)
     return a + b;
 }
 
-// Physical page holding logical page lp of the segment, or -1.
 // acc + the sum of the eight bf16 values in x, as four bf16 dot products with
 // (1, 1): the softmax denominator then sums exactly the rounded probabilities
 // that multiply V, in half the instructions of eight fp32 adds.
@@ -122,6 +121,7 @@ __device__ __forceinline__ float sum8_bf16(bf16x8 x, float acc)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
 }
 
+// Physical page holding logical page lp of the segment, or -1.
 __device__ __forceinline__ int page_id(const int32_t *__restrict__ pages, int n_pages, int64_t num_pages, int lp)
 {
     const int id = pages[min(max(lp, 0), n_pages - 1)];
@@ -129,38 +129,28 @@ __device__ __forceinline__ int page_id(const int32_t *__restrict__ pages, int n_
 }
 
 // Issue the loads of one KV tile (keys tile_key0 .. tile_key0+63 of the
-// segment) into registers. Every lane loads from a valid address; whether a
-// chunk may be used is recorded in st.ok and applied when the tile is
-// written to LDS, so the loads of a tile are all in flight together and
-// nothing waits on them here.
-//   BIG_PAGE (P >= 64): the tile lies inside one page whose id `tile_page`
-//   the caller loaded ahead of time (workgroup-uniform).
-//   otherwise: the tile spans 64 / P pages; each lane looks up its chunks'
-//   ids first (all id loads together), then issues its data loads.
-template <int D, bool BIG_PAGE>
+// segment) into registers. The tile spans 64 / P pages: each lane looks up
+// its chunks' page ids first (all id loads together), then issues its data
+// loads from valid addresses; whether a chunk may be used is recorded in
+// st.ok and applied when the tile is written to LDS, so the loads of a tile
+// are all in flight together and nothing waits on them here.
+template <int D>
 __device__ __forceinline__ void fetch_tile(Staged<D> &st, const u16 *__restrict__ kpool,
                                            const u16 *__restrict__ vpool, const int32_t *__restrict__ pages,
-                                           int32_t n_pages, int64_t num_pages, int log2P, int tile_key0,
-                                           int tile_page, int zero_lo, int zero_hi)
+                                           int32_t n_pages, int64_t num_pages, int log2P, int tile_key0, int zero_lo,
+                                           int zero_hi)
 {
     const int pmask = (1 << log2P) - 1;
     int kpage[Tile<D>::kPerThread], vpage[Tile<D>::vPerThread];
-    if constexpr (BIG_PAGE) {
 #pragma unroll
-        for (int r = 0; r < Tile<D>::kPerThread; ++r) kpage[r] = tile_page;
+    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        kpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + c / (D / 8)) >> log2P);
+    }
 #pragma unroll
-        for (int r = 0; r < Tile<D>::vPerThread; ++r) vpage[r] = tile_page;
-    } else {
-#pragma unroll
-        for (int r = 0; r < Tile<D>::kPerThread; ++r) {
-            const int c = threadIdx.x + r * kThreads;
-            kpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + c / (D / 8)) >> log2P);
-        }
-#pragma unroll
-        for (int r = 0; r < Tile<D>::vPerThread; ++r) {
-            const int c = threadIdx.x + r * kThreads;
-            vpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + (c % (kBK / 8)) * 8) >> log2P);
-        }
+    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        vpage[r] = page_id(pages, n_pages, num_pages, (tile_key0 + (c % (kBK / 8)) * 8) >> log2P);
     }
     unsigned ok = 0;
 #pragma unroll
@@ -218,66 +208,10 @@ __device__ __forceinline__ void store_tile(const Staged<D> &st, u16 *__restrict_
     }
 }
 
-// Fast path for a clean tile (page size >= 64, page present, every key of
-// the tile stored and visible to some query): each thread's chunks sit at
-// fixed byte offsets from a workgroup-uniform base, so a load is one
-// "SGPR base + VGPR offset" instruction and the LDS store needs no masking.
-template <int D>
-struct ChunkOffsets {
-    unsigned k[Tile<D>::kPerThread];  // bytes from the tile's first key in its K page
-    unsigned v[Tile<D>::vPerThread];  // bytes from the tile's first slot in its V page
-};
-
-template <int D>
-__device__ __forceinline__ ChunkOffsets<D> chunk_offsets(int log2P)
-{
-    ChunkOffsets<D> off;
-#pragma unroll
-    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
-        const int c = threadIdx.x + r * kThreads;
-        off.k[r] = static_cast<unsigned>(((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
-    }
-#pragma unroll
-    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
-        const int c = threadIdx.x + r * kThreads;
-        off.v[r] = static_cast<unsigned>((((c / (kBK / 8)) << log2P) + (c % (kBK / 8)) * 8) * 2);
-    }
-    return off;
-}
-
-template <int D>
-__device__ __forceinline__ void fetch_clean(Staged<D> &st, const u16 *__restrict__ kpool,
-                                            const u16 *__restrict__ vpool, int log2P, int page, int slot0,
-                                            const ChunkOffsets<D> &off)
-{
-    const char *kb = reinterpret_cast<const char *>(kpool) +
-                     ((static_cast<int64_t>(page) << log2P) + slot0) * static_cast<int64_t>(D * 2);
-    const char *vb = reinterpret_cast<const char *>(vpool) +
-                     (((static_cast<int64_t>(page) * D) << log2P) + slot0) * 2;
-#pragma unroll
-    for (int r = 0; r < Tile<D>::kPerThread; ++r) st.k[r] = *reinterpret_cast<const u32x4 *>(kb + off.k[r]);
-#pragma unroll
-    for (int r = 0; r < Tile<D>::vPerThread; ++r) st.v[r] = *reinterpret_cast<const u32x4 *>(vb + off.v[r]);
-}
-
-template <int D>
-__device__ __forceinline__ void store_clean(const Staged<D> &st, u16 *__restrict__ stage)
-{
-    u16 *ks = stage;
-    u16 *vs = stage + Tile<D>::kElems;
-#pragma unroll
-    for (int r = 0; r < Tile<D>::kPerThread; ++r) {
-        const int c = threadIdx.x + r * kThreads;
-        *reinterpret_cast<u32x4 *>(ks + (c / (D / 8)) * Tile<D>::kLd + (c % (D / 8)) * 8) = st.k[r];
-    }
-#pragma unroll
-    for (int r = 0; r < Tile<D>::vPerThread; ++r) {
-        const int c = threadIdx.x + r * kThreads;
-        *reinterpret_cast<u32x4 *>(vs + (c / (kBK / 8)) * Tile<D>::vLd + (c % (kBK / 8)) * 8) = st.v[r];
-    }
-}
-
-template <int D, int HPW, bool OUT_BF16, bool BIG_PAGE>
+// Register-staged kernel for pages shorter than a tile (16 or 32 keys): a
+// tile spans several pages, so each lane fetches its chunks into registers
+// and writes them to a padded LDS stage, with no cross-tile pipeline.
+template <int D, int HPW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
@@ -345,57 +279,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     for (int i = 0; i < kDBlocks; ++i) oacc[i] = f32x16{};
     float m = kNegBig, lsum = 0.f;
 
-    // Tile jt covers keys [64 jt, 64 jt + 64) of the segment. With BIG_PAGE it
-    // lies in logical page (64 jt) >> log2P. Page ids are read 64 at a time,
-    // one per lane, into a register window (the next window is loaded while the
-    // current one is in use), and a tile's id is taken from it with a lane read.
-    const int lp_first = (tile_beg * kBK) >> log2P;
-    int win = lp_first >> 6;
-    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
-    int win_cur = 0, win_next = 0;
-    if constexpr (BIG_PAGE) {
-        win_cur = load_window(win);
-        win_next = load_window(win + 1);
-    }
-    auto tile_page = [&](int jt) {
-        if constexpr (!BIG_PAGE) return 0;
-        const int lp = (jt * kBK) >> log2P;
-        if ((lp >> 6) != win) {  // tiles advance in order: step to the prefetched window
-            win = lp >> 6;
-            win_cur = win_next;
-            win_next = load_window(win + 1);
-        }
-        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
-        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
-    };
-    const ChunkOffsets<D> coff = chunk_offsets<D>(log2P);
-    // Fetch tile jt into st; returns whether it took the clean path.
+    // Tile jt covers keys [64 jt, 64 jt + 64) of the segment.
     auto fetch = [&](Staged<D> &st, int jt) {
-        const int page = tile_page(jt);
-        const int key0 = jt * kBK;
-        const bool clean = BIG_PAGE && page >= 0 && key0 >= zero_lo && key0 + kBK <= zero_hi;
-        if (clean)
-            fetch_clean<D>(st, kpool, vpool, log2P, page, (k_pos0 + key0) & ((1 << log2P) - 1), coff);
-        else
-            fetch_tile<D, BIG_PAGE>(st, kpool, vpool, pages, n_pages, num_pages, log2P, key0, page, zero_lo,
-                                    zero_hi);
-        return clean;
+        fetch_tile<D>(st, kpool, vpool, pages, n_pages, num_pages, log2P, jt * kBK, zero_lo, zero_hi);
     };
-    auto store = [&](const Staged<D> &st, bool clean, u16 *stage, int jt) {
-        if (clean)
-            store_clean<D>(st, stage);
-        else
-            store_tile<D>(st, stage, jt * kBK, zero_lo, zero_hi);
-    };
+    auto store = [&](const Staged<D> &st, u16 *stage, int jt) { store_tile<D>(st, stage, jt * kBK, zero_lo, zero_hi); };
     Staged<D> st;
-    store(st, fetch(st, tile_beg), smem, tile_beg);
+    fetch(st, tile_beg);
+    store(st, smem, tile_beg);
     __syncthreads();
 
     for (int jt = tile_beg; jt < tile_end; ++jt) {
         const int cur = (jt - tile_beg) & 1;
         const bool more = jt + 1 < tile_end;
-        bool clean_next = false;
-        if (more) clean_next = fetch(st, jt + 1);
+        if (more) fetch(st, jt + 1);
 
         const u16 *ks = smem + cur * T::stage;
         const u16 *vs = ks + T::kElems;
@@ -467,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
                 }
             }
         }
-        if (more) store(st, clean_next, smem + (cur ^ 1) * T::stage, jt + 1);
+        if (more) store(st, smem + (cur ^ 1) * T::stage, jt + 1);
         __syncthreads();
     }
 
@@ -887,6 +784,357 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
         }
     if (lse && half == 0)
         lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
+}
+
+// ---------------------------------------------------------------------------
+// Two-block prefill kernel (head dim 128, pages of at least one tile, units
+// of 256 (row, head) pairs). One wavefront per SIMD, each owning two
+// 32-column query blocks, so every K and V^T operand read from LDS feeds two
+// MFMAs: half the LDS operand traffic per FLOP of the one-block kernels,
+// whose two waves per SIMD each read their own copy of every operand (the
+// CU's LDS bandwidth, not the matrix cores, bounded those). The price is the
+// register state of 64 query columns: O^T (128 registers) and Q^T (64) live
+// in AGPRs as the MFMA accumulator and B operand, the scores of two tiles
+// (128) in VGPRs. That state is held in registers the compiler may not
+// allocate (the kernel's own code is limited to 64 VGPRs and 64 AGPRs) and
+// is touched only by the generated blocks of segkv_tile_asm.inc (written by
+// gen_tile_asm.py), which issue one tile's scores-of-the-next-tile, softmax
+// and P.V work in a fixed interleave. The loop around them (page ids, K/V
+// DMA into LDS, barriers, masking decisions) is the pipelined kernel's, with
+// four waves.
+constexpr unsigned kW2Lds = 4 * 16384;   // dynamic LDS of the two-block kernel: two K and two V^T tiles
+
+struct W2Addr {
+    unsigned ka[8];          // K operand of k-step s, K buffer 0 (LDS byte address)
+    unsigned va[4];          // V^T operand of 16-key step t, V buffer 0
+};
+
+// The blocks clobber registers above the kernel's own budget on purpose (that
+// is where their state lives), which clang reports for every block.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#include "segkv_tile_asm.inc"
+#pragma clang diagnostic pop
+
+template <int HPW, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void attn_prefill_w2_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
+    int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
+    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
+    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse, float *__restrict__ parts,
+    int32_t num_parts)
+{
+    constexpr int D = 128, NW = 4;
+    using T = DmaTile<D, NW>;
+    constexpr int kUnitRows = 256 / HPW;       // rows per unit (eight 32-row blocks over HPW heads)
+    constexpr int kBuf = 16384;                // one K or V^T tile
+    static_assert(T::kBytes == kBuf && T::vBytes == kBuf, "tile bodies assume 16 KB tiles");
+    // K buffers 0, 1 then V^T buffers 0, 1 (4 kBuf bytes of dynamic LDS): the
+    // tile bodies address buffer 1 as buffer 0 plus kBuf. The LDS is dynamic
+    // so that the compiler's occupancy estimate does not raise the kernel's
+    // own register budget into the range the tile bodies keep their state in.
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    char *const kbuf0 = smem, *const kbuf1 = smem + kBuf, *const vbuf0 = smem + 2 * kBuf,
+               *const vbuf1 = smem + 3 * kBuf;
+
+    const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
+    const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
+    const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
+    const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
+    const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
+    const int part = unit2[SEGKV_UNIT_PART - 4];
+    if (seg < 0 || seg >= num_segments || part >= num_parts) return;
+    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
+    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
+    int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
+    if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
+    const int32_t *pages = page_list + page_off;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    // The wave's two blocks: consecutive 32-row blocks of one head, or (eight
+    // heads per unit) one 32-row block of two heads.
+    int hoff[2], rblk[2];
+    if constexpr (HPW == 8) {
+        hoff[0] = 2 * wave, hoff[1] = 2 * wave + 1, rblk[0] = rblk[1] = 0;
+    } else {
+        hoff[0] = hoff[1] = wave % HPW;
+        rblk[0] = 2 * (wave / HPW), rblk[1] = 2 * (wave / HPW) + 1;
+    }
+
+    const int unit_end = min(row0 + kUnitRows, n_q);
+    const int first_pos = q_pos0 + row0, last_pos = q_pos0 + unit_end - 1;
+    const int lo_pos = window ? max(0, first_pos - window + 1) : 0;
+    const int tile_beg = max((lo_pos - k_pos0) / kBK, run0);
+    const int tile_end = min((last_pos + 1 - k_pos0 + kBK - 1) / kBK, run0 + max(run_len, 0));
+    const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
+    const int zero_hi = k_len;
+
+    // Per block: rows, positions, and whether the block exists.
+    int wrow0[2], my_pos[2], lo_i[2], head[2];
+    int64_t my_row[2];
+    bool blk_ok[2], row_ok[2];
+    int wr_first = 1 << 30, wr_last = -1;   // the wave's valid rows (relative to the segment)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        head[k] = head0 + hoff[k];
+        wrow0[k] = row0 + rblk[k] * kWaveRows;
+        blk_ok[k] = wrow0[k] < n_q && head[k] < hq;
+        const int my_t = min(wrow0[k] + col, n_q - 1);
+        my_pos[k] = q_pos0 + my_t;
+        lo_i[k] = window ? my_pos[k] - window + 1 : -(1 << 30);
+        my_row[k] = static_cast<int64_t>(q_row0) + my_t;
+        row_ok[k] = blk_ok[k] && (wrow0[k] + col) < n_q && my_row[k] < total_q_rows;
+        if (blk_ok[k]) {
+            wr_first = min(wr_first, wrow0[k]);
+            wr_last = max(wr_last, min(wrow0[k] + kWaveRows, n_q) - 1);
+        }
+    }
+    const int wp_lo = q_pos0 + wr_first, wp_hi = q_pos0 + wr_last;
+
+    // Q^T of both blocks into its AGPRs, one 16-byte chunk at a time; O^T = 0.
+    auto set_q = [&](auto qb_c) {
+        constexpr int k = decltype(qb_c)::value;
+        const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
+        const u16 *qp = q + (my_row[k] * hq + min(head[k], hq - 1)) * D + 8 * half;
+        auto chunk = [&](auto s_c) {
+            constexpr int s = decltype(s_c)::value;
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+            w2_set_q<k, s>(raw[0], raw[1], raw[2], raw[3]);
+        };
+        chunk(std::integral_constant<int, 0>{});
+        chunk(std::integral_constant<int, 1>{});
+        chunk(std::integral_constant<int, 2>{});
+        chunk(std::integral_constant<int, 3>{});
+        chunk(std::integral_constant<int, 4>{});
+        chunk(std::integral_constant<int, 5>{});
+        chunk(std::integral_constant<int, 6>{});
+        chunk(std::integral_constant<int, 7>{});
+    };
+    set_q(std::integral_constant<int, 0>{});
+    set_q(std::integral_constant<int, 1>{});
+    w2_zero_o();
+    float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;   // running maximum (log2 domain) and sum per block
+
+    int win = ((tile_beg * kBK) >> log2P) >> 6;
+    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
+    int win_cur = load_window(win), win_next = load_window(win + 1);
+    auto tile_page = [&](int jt) {
+        const int lp = (jt * kBK) >> log2P;
+        if ((lp >> 6) != win) {
+            win = lp >> 6;
+            win_cur = win_next;
+            win_next = load_window(win + 1);
+        }
+        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
+        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    };
+
+    unsigned kdma[T::kInstr], vdma[T::vInstr];
+#pragma unroll
+    for (int i = 0; i < T::kInstr; ++i) {
+        const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
+        const int rr = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(rr);
+        kdma[i] = static_cast<unsigned>(rr * T::kRowBytes + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < T::vInstr; ++i) {
+        const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
+        const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
+        vdma[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
+    }
+    auto dma_k = [&](char *dst, int page, int jt) {
+        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
+        const int64_t pg = page >= 0 ? page : 0;
+        const __amdgpu_buffer_rsrc_t rk =
+            page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
+#pragma unroll
+        for (int i = 0; i < T::kInstr; ++i)
+            dma16(rk, dst + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+    };
+    auto dma_v = [&](char *dst, int page, int jt) {
+        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
+        const int64_t pg = page >= 0 ? page : 0;
+        const __amdgpu_buffer_rsrc_t rv = page_rsrc(vpool + ((pg * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
+#pragma unroll
+        for (int i = 0; i < T::vInstr; ++i)
+            dma16(rv, dst + (wave * T::vInstr + i) * 1024, vdma[i], slot0 * 2);
+    };
+    auto edge_tile = [&](int jt) {
+        const int key0 = jt * kBK;
+        return key0 < zero_lo || key0 + kBK > zero_hi;
+    };
+    auto fixup = [&](char *vb, int jt) {
+        const int key0 = jt * kBK;
+        for (int e = threadIdx.x; e < D * kBK; e += NW * 64) {
+            const int d = e / kBK, k = e % kBK, idx = key0 + k;
+            if (idx < zero_lo || idx >= zero_hi)
+                *reinterpret_cast<u16 *>(vb + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
+        }
+    };
+
+    // LDS operand addresses (buffer 0; the tile bodies add the buffer and
+    // 32-row block offsets as instruction offsets).
+    W2Addr ad;
+    {
+        const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem));
+        const int krow = swizzle_row(col);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            ad.ka[s] = base + static_cast<unsigned>(krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            ad.va[t] = base + 2 * kBuf + static_cast<unsigned>(col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
+    }
+
+    auto tile_full = [&](int jt) {
+        const int kp0 = k_pos0 + jt * kBK;
+        return (kp0 + kBK - 1 <= wp_lo) && (window == 0 || kp0 >= wp_hi - window + 1);
+    };
+    // Mask operands of tile jt: visible iff (key - lo_i) <= (pos - lo_i), unsigned.
+    auto mask_args = [&](int jt, int k, int &a, unsigned &s) {
+        const int kbase = k_pos0 + jt * kBK + 8 * half;
+        a = lo_i[k] - kbase;
+        s = static_cast<unsigned>(my_pos[k] - lo_i[k]);
+    };
+    auto mask_x = [&](int jt) {
+        int a0, a1;
+        unsigned s0, s1;
+        mask_args(jt, 0, a0, s0);
+        mask_args(jt, 1, a1, s1);
+        w2_mask_x(a0, s0, a1, s1, __builtin_amdgcn_readfirstlane(tile_full(jt) ? 1u : 0u));
+    };
+    auto mask_y = [&](int jt) {
+        int a0, a1;
+        unsigned s0, s1;
+        mask_args(jt, 0, a0, s0);
+        mask_args(jt, 1, a1, s1);
+        w2_mask_y(a0, s0, a1, s1, __builtin_amdgcn_readfirstlane(tile_full(jt) ? 1u : 0u));
+    };
+
+    // Iteration jt, parity A: scores of jt in X, next into Y from K buffer 1,
+    // V^T(jt) in buffer 0; meanwhile V(jt+1) is DMA'd into V buffer 1 and
+    // K(jt+2) into K buffer 0. Parity B mirrors it. A unit's last tile runs
+    // the variant without next scores.
+    if (tile_beg < tile_end) {
+        int page_v = -1;   // page of tile jt + 1, looked up when its K was fetched
+        const int page0 = tile_page(tile_beg);
+        dma_k(kbuf0, page0, tile_beg);
+        dma_v(vbuf0, page0, tile_beg);
+        if (tile_beg + 1 < tile_end) {
+            page_v = tile_page(tile_beg + 1);
+            dma_k(kbuf1, page_v, tile_beg + 1);
+        }
+        __syncthreads();
+        if (edge_tile(tile_beg)) fixup(vbuf0, tile_beg);
+        w2_scores_first(ad, scale_log2);
+        __syncthreads();   // kbuf0 is refilled by the first iteration; the V fixup is visible
+        for (int jt = tile_beg;; jt += 2) {
+            if (jt + 1 >= tile_end) {
+                mask_x(jt);
+                w2_last_x(m0, m1, l0, l1, ad, scale_log2);
+                break;
+            }
+            dma_v(vbuf1, page_v, jt + 1);
+            if (jt + 2 < tile_end) {
+                page_v = tile_page(jt + 2);
+                dma_k(kbuf0, page_v, jt + 2);
+            }
+            mask_x(jt);
+            w2_tile_xy(m0, m1, l0, l1, ad, scale_log2);
+            __syncthreads();
+            if (edge_tile(jt + 1)) {
+                fixup(vbuf1, jt + 1);
+                __syncthreads();
+            }
+            if (jt + 2 >= tile_end) {
+                mask_y(jt + 1);
+                w2_last_y(m0, m1, l0, l1, ad, scale_log2);
+                break;
+            }
+            dma_v(vbuf0, page_v, jt + 2);
+            if (jt + 3 < tile_end) {
+                page_v = tile_page(jt + 3);
+                dma_k(kbuf1, page_v, jt + 3);
+            }
+            mask_y(jt + 1);
+            w2_tile_yx(m0, m1, l0, l1, ad, scale_log2);
+            __syncthreads();
+            if (edge_tile(jt + 2)) {
+                fixup(vbuf0, jt + 2);
+                __syncthreads();
+            }
+        }
+    }
+
+    // Epilogue: lane (col, half) holds O^T dims 32 db + 8 j + 4 half + i of its
+    // column of block k as the four values w2_get_o<k, db, j> returns.
+    w2_drain();
+    const float ltot[2] = {sum_halves(l0), sum_halves(l1)};
+    const float mfin[2] = {m0, m1};
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    auto finish = [&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        float4 v[4][4];
+        auto get = [&](auto db_c, auto j_c) {
+            constexpr int db = decltype(db_c)::value, j = decltype(j_c)::value;
+            w2_get_o<k, db, j>(v[db][j].x, v[db][j].y, v[db][j].z, v[db][j].w);
+        };
+        auto get_db = [&](auto db_c) {
+            get(db_c, std::integral_constant<int, 0>{});
+            get(db_c, std::integral_constant<int, 1>{});
+            get(db_c, std::integral_constant<int, 2>{});
+            get(db_c, std::integral_constant<int, 3>{});
+        };
+        get_db(std::integral_constant<int, 0>{});
+        get_db(std::integral_constant<int, 1>{});
+        get_db(std::integral_constant<int, 2>{});
+        get_db(std::integral_constant<int, 3>{});
+        if (part >= 0) {
+            constexpr int kPairs = kUnitRows * HPW;
+            float *slot = parts + static_cast<int64_t>(part) * (kPairs * (D + 2));
+            const int rr = hoff[k] * kUnitRows + rblk[k] * kWaveRows + col;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    *reinterpret_cast<f32x4 *>(slot + rr * D + 32 * db + 8 * jj + 4 * half) =
+                        f32x4{v[db][jj].x, v[db][jj].y, v[db][jj].z, v[db][jj].w};
+            if (half == 0) {
+                slot[kPairs * D + rr] = mfin[k];
+                slot[kPairs * (D + 1) + rr] = ltot[k];
+            }
+            return;
+        }
+        if (!row_ok[k]) return;
+        const float inv = ltot[k] > 0.f ? 1.0f / ltot[k] : 0.f;
+        const int64_t obase = (my_row[k] * hq + head[k]) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * db + 8 * jj + 4 * half;
+                const float v0 = v[db][jj].x * inv, v1 = v[db][jj].y * inv;
+                const float v2 = v[db][jj].z * inv, v3 = v[db][jj].w * inv;
+                if constexpr (OUT_BF16) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) =
+                        bf16x4{static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
+                               static_cast<__bf16>(v3)};
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
+                }
+            }
+        if (lse && half == 0)
+            lse[static_cast<int64_t>(head[k]) * total_q_rows + my_row[k]] =
+                (mfin[k] + __log2f(ltot[k])) * 0.69314718055994530942f;
+    };
+    finish(std::integral_constant<int, 0>{});
+    finish(std::integral_constant<int, 1>{});
 }
 
 // Decode / small-chunk kernel (pages of at least one tile). A unit is one
@@ -1473,58 +1721,70 @@ int log2_of(int p)
 }
 
 template <int D, int HPW, bool OUT_BF16>
-void launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
-            float *parts, hipStream_t stream)
+int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
+           float *parts, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(t.num_units)), block(kThreads);
     const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
     const u16 *vp = static_cast<const u16 *>(cfg.v_pool);
     const int log2P = log2_of(cfg.page_size);
-    if (cfg.page_size >= kBK && t.unit_rows * t.unit_heads <= kWaveRows)
+    const bool big_page = cfg.page_size >= kBK;
+    if (big_page && t.unit_rows * t.unit_heads <= kWaveRows) {
         hipLaunchKernelGGL((attn_decode_kernel<D, OUT_BF16>), grid, dim3(kDecThreads), 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
                            t.num_segments, t.total_q_rows, cfg.num_q_heads, t.unit_rows, t.unit_heads, scale_log2,
                            o, lse, parts, t.num_parts);
-    else if (cfg.page_size >= kBK && t.unit_rows * t.unit_heads == kWideWaves * kWaveRows)
-        hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWideWaves>), grid, dim3(kWideWaves * 64), 0,
-                           stream, qh, kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries,
-                           t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts,
-                           t.num_parts);
-    else if constexpr (HPW > kWaves)
-        return;   // eight heads per unit exist only in eight-wave units
-    else if (cfg.page_size >= kBK)
+    } else if (t.unit_heads != HPW) {
+        // decode units take any G heads; every prefill kernel is built per heads-per-unit
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: unsupported unit_heads %d", t.unit_heads);
+    } else if (big_page && t.unit_rows * t.unit_heads == kWideWaves * kWaveRows) {
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((attn_prefill_w2_kernel<HPW, OUT_BF16>), grid, dim3(4 * 64), kW2Lds, stream, qh, kp, vp,
+                               cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
+                               t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts,
+                               t.num_parts);
+        else
+            hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWideWaves>), grid, dim3(kWideWaves * 64),
+                               0, stream, qh, kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list,
+                               t.num_page_entries, t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads,
+                               scale_log2, o, lse, parts, t.num_parts);
+    } else if constexpr (HPW > kWaves) {
+        // eight heads per unit exist only in eight-wave (256-pair) units
+        return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: %d heads per unit need units of %d pairs (tables have %d)",
+                    HPW, kWideWaves * kWaveRows, t.unit_rows * t.unit_heads);
+    } else if (big_page) {
         hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWaves>), grid, block, 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts, t.num_parts);
-    else
-        hipLaunchKernelGGL((attn_prefill_kernel<D, HPW, OUT_BF16, false>), grid, block, 0, stream, qh, kp, vp,
+    } else {
+        hipLaunchKernelGGL((attn_prefill_kernel<D, HPW, OUT_BF16>), grid, block, 0, stream, qh, kp, vp,
                            cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work, t.num_segments,
                            t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse);
+    }
     if (t.num_merges > 0)
         hipLaunchKernelGGL((merge_parts_kernel<D, OUT_BF16>), dim3(static_cast<unsigned>(t.num_merges), kMergeDSplit),
                            block, 0, stream, t.merge, parts, t.num_parts, t.unit_rows, t.unit_heads, t.total_q_rows,
                            cfg.num_q_heads, o, lse);
+    return SEGKV_OK;
 }
 
 template <int D, int HPW>
-void launch_dtype(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                  float *lse, float scale_log2, float *parts, hipStream_t stream)
+int launch_dtype(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
+                 float *lse, float scale_log2, float *parts, hipStream_t stream)
 {
-    if (o_dtype == SEGKV_DTYPE_BF16)
-        launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, parts, stream);
-    else
-        launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, parts, stream);
+    if (o_dtype == SEGKV_DTYPE_BF16) return launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, parts, stream);
+    return launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, parts, stream);
 }
 
 template <int D>
-void launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                  float *lse, float scale_log2, float *parts, hipStream_t stream)
+int launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
+                 float *lse, float scale_log2, float *parts, hipStream_t stream)
 {
     switch (t.unit_heads) {
-    case 8: launch_dtype<D, 8>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
-    case 4: launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
-    case 2: launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
-    default: launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream); break;
+    case 8: return launch_dtype<D, 8>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
+    case 4: return launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
+    case 2: return launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
+    default: return launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
     }
 }
 
@@ -1562,6 +1822,7 @@ int launch_attn_mass(const segkv_config &cfg, const segkv_dev_tables &t, const v
                      float scale_log2, float *mass, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated call is not this call's
     const int64_t n = t.total_q_rows;
     const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
     if (n > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, s, mass, n);
@@ -1581,10 +1842,10 @@ int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, cons
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     float *parts = static_cast<float *>(workspace);
-    if (cfg.head_dim == 128)
-        launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
-    else
-        launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated call is not this call's
+    const int rc = cfg.head_dim == 128 ? launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s)
+                                       : launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
+    if (rc != SEGKV_OK) return rc;
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: %s", hipGetErrorString(err));
     return SEGKV_OK;

@@ -138,6 +138,12 @@ WIDE = [
     (4, 2, 64, 128, 3000, (1, 0), ((2500, 200), (4000, 77)), 0),
     (2, 2, 128, 256, 0, (1, 1), ((2100, 513),), 3),
     (16, 2, 128, 64, 2500, (0, 1), ((5000, 100), (2200, 33)), 0),
+    # G = 4 and G = 2 at head dim 128: the two-block kernel with 4 x 64 and
+    # 2 x 128 units (G = 4 is the 128K stack's shape)
+    (8, 2, 128, 64, 1500, (1, 0), ((2500, 333),), 0),
+    (8, 2, 128, 64, 2200, (0, 1), ((3000, 200), (2100, 65)), 5),
+    (4, 2, 128, 64, 0, (1, 1), ((2049, 130),), 0),
+    (4, 1, 128, 128, 2100, (0,), ((2500, 700),), 0),
 ]
 
 
@@ -232,7 +238,10 @@ def test_stack128k_sampled_layers():
 
 
 @pytest.mark.parametrize("w", [TINY, adhoc(hq=8, hkv=2, d=128, page=64, window=100, classes=(0, 1),
-                                            seqs=((0, 200), (37, 301)), seed=9)], ids=["tiny", "ragged"])
+                                            seqs=((0, 200), (37, 301)), seed=9),
+                               adhoc(hq=8, hkv=2, d=128, page=64, window=1500, classes=(1, 0),
+                                     seqs=((2500, 333),), seed=19)],
+                         ids=["tiny", "ragged", "wide_g4"])
 def test_bitwise_invariances(w):
     r = realize(w)
     t = layer_tensors(w, r, 0, device="cuda")
