@@ -23,14 +23,24 @@ scalars (running maximum and sum, addresses, the scale) pass through
 operands. The state therefore survives any code the compiler places between
 the blocks. The blocks issue the tile in a fixed interleave:
 
-  * the scores of tile j+1 (32 MFMAs) are computed while tile j's scores
-    become probabilities (running maximum, exp2, bf16 packing, row sums) and
-    are multiplied into O^T (32 MFMAs);
+  * tile j's scores become probabilities (exp2 against the running maximum,
+    bf16 packing, row sums) and are multiplied into O^T (32 MFMAs) while the
+    scores of tile j+1 are computed (32 MFMAs); once those are done, the
+    same body masks them (edge tiles only), takes their maximum and applies
+    the running-maximum refresh, so the next body starts on its
+    exponentials at once, with no branch among its MFMAs;
   * LDS operand reads run a few operands ahead through a small register ring,
     with counted lgkmcnt waits;
+  * the K and V^T tiles are staged in a three-slot LDS ring: each tile body
+    issues the DMA of the K tile three ahead and the V^T tile two ahead
+    (eight buffer_load ... lds instructions, spread between its first MFMAs,
+    the source page and destination slot passed in) and ends with a wait for
+    the previous tile's DMA only (vmcnt(8)) and the workgroup barrier, so the
+    copies have more than a tile's time to land and their issue hides
+    behind the matrix cores;
   * the running-maximum refresh (rare: only when a tile's maximum exceeds the
-    running one by more than the slack) is a wave-uniform branch inside the
-    block.
+    running one by more than the slack) is a wave-uniform branch at the end
+    of the body, just before the barrier.
 
 Register map (fixed; v0..v63 and a0..a63 belong to the compiler):
   a[64:191]   O^T: block qb, 32-dim block db at a[64 + 64 qb + 16 db : +15]
@@ -39,14 +49,17 @@ Register map (fixed; v0..v63 and a0..a63 belong to the compiler):
               at base + 32 qb + 16 kb; after the softmax, the bf16
               probabilities of 16-key step t sit at base + 32 qb + 16 (t/2) +
               8 (t%2) : +3 (written in place)
-  v[64:87]    operand ring (six 4-register slots; v[88:115] unused)
+  v[64:87]    operand ring (six 4-register slots)
+  v[88:99]    this tile's LDS operand addresses (K slot + lane offset per
+              k-step, V^T slot + lane offset per 16-key step)
   v[116:127]  temporaries
 
 Hazards handled here (the compiler's hazard recognizer does not look inside
 inline assembly): MFMA results are read by VALU code only a tile later or
-after explicit s_nop padding; VALU-written probabilities reach an MFMA only
-after at least two other instructions; a transcendental result is never read
-by the next instruction; v_permlane32_swap is padded on both sides.
+after at least HAZ_MFMA_VALU other instructions; VALU-written probabilities
+reach an MFMA only after at least two other instructions; a transcendental
+result is never read by the next instruction; v_permlane32_swap is padded on
+both sides; M0 is written one instruction before the DMA that reads it.
 """
 
 import math
@@ -62,15 +75,16 @@ OWN = 64                    # registers below this index are the compiler's
 RING0, NRING = 64, 6        # operand ring v[64:87]
 TMP0 = 116                  # temporaries v116..v127
 LOOKAHEAD = 4               # operand reads issued this many operands ahead
-KBUF_BYTES = 16384          # one K or V^T tile in LDS
+KADDR, VADDR = 88, 96       # per-tile LDS operand addresses
+DMA_AFTER = (1, 3, 5, 7, 9, 11, 13, 15)   # the tile's DMA instructions follow these MFMAs
 KB_BYTES = 32 * 256         # 32 K rows of 128 bf16
 DB_BYTES = 32 * 128         # 32 V^T rows of 64 bf16
-ONES_BF16X2 = "0x3f803f80"  # (1.0, 1.0) in bf16
 NEG_INF = "0xff800000"
 SLACK_LOG2 = "0x41000000"   # 8.0: refresh the running maximum only beyond this
-# S MFMA operands issued before each group of P.V operands (t = 0..3); the
-# rest of the 16 K operands go first.
-S_SPLIT = (9, 3, 2, 2)
+# K operands (two S MFMAs each) issued before each group of P.V operands
+# (t = 0..3); the 16 K operands in total.
+S_SPLIT = (6, 5, 5, 0)
+HAZ_MFMA_VALU = 12          # instructions between an MFMA and a VALU read of its result
 
 
 def T(i):
@@ -106,13 +120,33 @@ class Operand:
         return self.b if self.kind == "V" else None
 
 
-def read_text(op, slot, kbuf, vbuf):
+def read_text(op, slot):
     r = RING0 + 4 * slot
     if op.kind == "K":
         kb, s = op.a, op.b
-        return f"ds_read_b128 {vblk(r, 4)}, %[ka{s}] offset:{kbuf * KBUF_BYTES + kb * KB_BYTES}"
+        return f"ds_read_b128 {vblk(r, 4)}, v{KADDR + s} offset:{kb * KB_BYTES}"
     db, t = op.a, op.b
-    return f"ds_read_b128 {vblk(r, 4)}, %[va{t}] offset:{vbuf * KBUF_BYTES + db * DB_BYTES}"
+    return f"ds_read_b128 {vblk(r, 4)}, v{VADDR + t} offset:{db * DB_BYTES}"
+
+
+def addr_lines(k=True, v=True):
+    """This tile's operand addresses: lane offsets plus the slot's LDS address."""
+    out = []
+    if k:
+        out += [f"v_add_u32 v{KADDR + s}, %[kslot], %[ka{s}]" for s in range(8)]
+    if v:
+        out += [f"v_add_u32 v{VADDR + t}, %[vslot], %[va{t}]" for t in range(4)]
+    return out
+
+
+def dma_lines(i):
+    """DMA instruction i of the tile (0-3: the K tile, 4-7: the V^T tile), 1 KB
+    per wave instruction: lane l's 16 bytes land at M0 + 16 l."""
+    if i < 4:
+        return [f"s_add_u32 m0, %[m0k], {i * 1024}", "s_nop 0",
+                f"buffer_load_dwordx4 %[kd{i}], %[rk], %[sok] offen lds"]
+    return [f"s_add_u32 m0, %[m0v], {(i - 4) * 1024}", "s_nop 0",
+            f"buffer_load_dwordx4 %[vd{i - 4}], %[rv], %[sov] offen lds"]
 
 
 def mfma_texts(op, slot, cur, nxt):
@@ -133,15 +167,39 @@ def mfma_texts(op, slot, cur, nxt):
     return out
 
 
-def max_items(cur):
-    """Running maximum of both blocks: per block two chains of three-operand
-    maxima, the cross-half exchange, the scale; then the refresh test."""
+def mask_block(s_set):
+    """Scores of keys outside [lo_i, pos_i] of their query become -inf:
+    element (kb, e) of block qb holds key c + 8 half + tile start, visible iff
+    c - a_qb <= span_qb (unsigned), a_qb = lo_i - tile start - 8 half.
+    Skipped as a whole when the wave-uniform flag `full` is set (every key of
+    the tile visible to every row of the wave)."""
+    lines = ["s_cmp_lg_u32 %[full], 0",
+             "s_cbranch_scc1 .Lw2full_%=",
+             f"v_mov_b32 {T(8)}, {NEG_INF}"]
+    k = 0
+    for qb in range(2):
+        for kb in range(2):
+            for e in range(16):
+                t = T(9 + (k & 1))
+                r = f"v{sreg(s_set, qb, kb, e)}"
+                lines += [f"v_sub_u32 {t}, {key_const(kb, e)}, %[a{qb}]",
+                          f"v_cmp_le_u32 vcc, {t}, %[s{qb}]",
+                          f"v_cndmask_b32 {r}, {T(8)}, {r}, vcc"]
+                k += 1
+    lines.append(".Lw2full_%=:")
+    return "\n".join(lines)
+
+
+def max_items(s_set):
+    """Maxima of both blocks of a tile's scores: per block two chains of
+    three-operand maxima (NaN-propagating), the exchange between the two
+    32-lane halves, and the scale into the log2 domain (T4, T5)."""
     items = []
     for qb in range(2):
         ta, tb = T(2 * qb), T(2 * qb + 1)
         chains = []
         for kb, dst in ((0, ta), (1, tb)):
-            regs = [f"v{sreg(cur, qb, kb, e)}" for e in range(16)]
+            regs = [f"v{sreg(s_set, qb, kb, e)}" for e in range(16)]
             ops = [f"v_maximum3_f32 {dst}, {regs[0]}, {regs[1]}, {regs[2]}"]
             i = 3
             while i < 16:
@@ -162,16 +220,16 @@ def max_items(cur):
     return items
 
 
-def rescale_block():
-    """Taken when some lane's tile maximum exceeds its running maximum by
+def refresh_block():
+    """When some lane's tile maximum (T4, T5) exceeds its running maximum by
     more than the slack: m = max(m, mt), alpha = 2^(m_old - m), l and O^T
-    scaled by alpha."""
+    scaled by alpha. Wave-uniform branch; O^T may still be being written by
+    the body's last P.V MFMAs, hence the padding before reading it."""
     lines = [f"v_sub_f32 {T(6)}, {T(4)}, %[m0]",
              f"v_sub_f32 {T(7)}, {T(5)}, %[m1]",
              f"v_max_f32 {T(6)}, {T(6)}, {T(7)}",
              f"v_cmp_lt_f32 vcc, {SLACK_LOG2}, {T(6)}",
              "s_cbranch_vccz .Lw2keep_%=",
-             # the previous tile's P.V MFMAs may still be writing O^T
              "s_nop 7", "s_nop 7", "s_nop 7",
              f"v_max_f32 {T(0)}, %[m0], {T(4)}",
              f"v_max_f32 {T(1)}, %[m1], {T(5)}",
@@ -193,159 +251,181 @@ def rescale_block():
     return "\n".join(lines)
 
 
-def exp_items(cur, qb, t):
+def exp_items(s_set, qb, t):
     """p = 2^(s * scale - m) for the 8 scores of 16-key step t of block qb,
-    packed in place to the bf16 P^T operand, and added to the row sum."""
-    base = sreg(cur, qb, t >> 1, 8 * (t & 1))
+    added to the row sum in fp32 and packed in place to the bf16 P^T operand."""
+    base = sreg(s_set, qb, t >> 1, 8 * (t & 1))
     f = [(f"v_fma_f32 v{base + i}, v{base + i}, %[scale], -%[m{qb}]", 1) for i in range(8)]
     e = [(f"v_exp_f32 v{base + i}, v{base + i}", 2) for i in range(8)]
-    order = [f[0], f[1], f[2], f[3], e[0], f[4], e[1], f[5], e[2], f[6], e[3], f[7], e[4], e[5], e[6], e[7]]
+    a = [(f"v_add_f32 %[l{qb}], %[l{qb}], v{base + i}", 1) for i in range(8)]
     cvt = [(f"v_cvt_pk_bf16_f32 v{base + k}, v{base + 2 * k}, v{base + 2 * k + 1}", 1) for k in range(4)]
-    dot = [(f"v_dot2c_f32_bf16 %[l{qb}], {ONES_BF16X2}, v{base + k}", 1) for k in range(4)]
-    return order + cvt + dot
+    # no result of a transcendental is read by the next instruction
+    order = [f[0], f[1], f[2], f[3], e[0], f[4], e[1], f[5], e[2], f[6], e[3], f[7], e[4], a[0], e[5], a[1],
+             e[6], a[2], e[7], a[3], a[4], a[5], a[6], a[7], cvt[0], cvt[1], cvt[2], cvt[3]]
+    return order
 
 
-def tile_body(cur, nxt, kbuf, vbuf):
-    """One tile: softmax and P.V of the scores in set `cur` (V^T from buffer
-    vbuf); with nxt, the next tile's scores into set `nxt` from K buffer kbuf."""
-    s_ops = [Operand("K", kb, s) for s in range(8) for kb in range(2)] if nxt is not None else []
+def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail):
+    """Interleave the MFMA operand stream `ops` with
+      exp_q:  (text, weight, t) items, all of step t due before its first P.V MFMA;
+      post_q: (text, weight) items that read the scores of the next tile, so
+              only once every S MFMA of the body is HAZ_MFMA_VALU instructions
+              old;
+      final:  lines after the last MFMA and the queues (the refresh);
+    plus the LDS operand reads (LOOKAHEAD operands ahead), the DMA
+    instructions after the MFMAs listed in DMA_AFTER, and `tail`. Beside each
+    MFMA goes an even share of the remaining VALU weight, exponentials first
+    whenever their deadline needs them."""
+    lines = []
+    n = len(ops)
+    slots = [i % NRING for i in range(n)]
+    s_idx = [i for i, o in enumerate(ops) if o.kind == "K"]
+    last_s = s_idx[-1] if s_idx else -1
+    done_at = {}
+    for i, v in enumerate(exp_q):
+        done_at[v[2]] = i + 1
+    ei = pi = 0                # next exp / post item
+    s_end_at = None            # line count after the last S MFMA
+    p_written = {}             # P operand base register -> line index of its last write
+    mfma_no = 0
+    pending_dma = list(dma)
+
+    def post_ready():
+        return s_end_at is not None and len(lines) - s_end_at >= HAZ_MFMA_VALU
+
+    def take_exp():
+        nonlocal ei
+        text, wt, t = exp_q[ei]
+        lines.extend(text.split("\n"))
+        if text.startswith("v_cvt_pk_bf16_f32"):
+            reg = int(text.split()[1].lstrip("v").rstrip(","))
+            p_written[reg - (reg - cur) % 4] = len(lines)
+        ei += 1
+        return wt
+
+    def take_post():
+        nonlocal pi
+        text, wt = post_q[pi]
+        lines.extend(text.split("\n"))
+        pi += 1
+        return wt
+
+    issued = 0
+    for i in range(min(LOOKAHEAD, n)):
+        lines.append(read_text(ops[i], slots[i]))
+        issued += 1
+    for i, op in enumerate(ops):
+        if op.exp_t is not None:
+            while ei < done_at.get(op.exp_t, 0):
+                take_exp()
+            for qb in range(2):
+                base = sreg(cur, qb, op.exp_t >> 1, 8 * (op.exp_t & 1))
+                if len(lines) - p_written.get(base, -10) < 2:
+                    lines.append("s_nop 1")
+                    break
+        lines.append(f"s_waitcnt lgkmcnt({min(issued - 1 - i, 15)})")
+        for k, mt in enumerate(mfma_texts(op, slots[i], cur, nxt)):
+            lines.append(mt)
+            mfma_no += 1
+            if k == 0 and i + LOOKAHEAD < n:
+                j = i + LOOKAHEAD
+                lines.append(read_text(ops[j], slots[j]))
+                issued += 1
+            if k == 1 and i == last_s:
+                s_end_at = len(lines)
+            if pending_dma and mfma_no - 1 >= DMA_AFTER[len(dma) - len(pending_dma)]:
+                lines.extend(dma_lines(pending_dma.pop(0)))
+            # this slot's share
+            left = 2 * n - mfma_no + 1
+            rest_exp = sum(v[1] for v in exp_q[ei:])
+            rest_post = sum(v[1] for v in post_q[pi:])
+            share = math.ceil((rest_exp + rest_post) / left)
+            # exponentials the next deadline needs by now
+            need = 0
+            nxt_t = next((o.exp_t for o in ops[i + 1:] if o.exp_t is not None and ei < done_at[o.exp_t]), None)
+            if nxt_t is not None:
+                dl = next(j for j in range(i + 1, n) if ops[j].exp_t == nxt_t)
+                slots_left = 2 * (dl - i) - (1 if k == 0 else 0) - 1
+                due = sum(v[1] for v in exp_q[ei:done_at[nxt_t]])
+                need = math.ceil(due / max(slots_left, 1))
+            w = 0
+            while w < need and ei < len(exp_q):
+                w += take_exp()
+            while w < share and (ei < len(exp_q) or (pi < len(post_q) and post_ready())):
+                if pi < len(post_q) and post_ready():
+                    w += take_post()
+                else:
+                    w += take_exp()
+    while ei < len(exp_q):
+        take_exp()
+    while pi < len(post_q):
+        if not post_ready():
+            lines.append("s_nop 7")
+            continue
+        take_post()
+    assert not pending_dma
+    lines.extend(final)
+    lines.extend(tail)
+    return lines
+
+
+def s_ops():
+    return [Operand("K", kb, s) for s in range(8) for kb in range(2)]
+
+
+def tile_body(cur, nxt):
+    """One tile: softmax and P.V of the scores in set `cur`; with nxt, the
+    next tile's scores into set `nxt` (then masked, their maximum taken and
+    the running maximum refreshed), the DMA of later tiles, and the wait +
+    barrier that end the tile."""
+    ks = s_ops() if nxt is not None else []
     pv = [[Operand("V", db, t) for db in range(4)] for t in range(4)]
     ops = []
     pos = 0
     for t in range(4):
-        take = S_SPLIT[t] if s_ops else 0
-        ops += s_ops[pos:pos + take]
+        take = S_SPLIT[t] if ks else 0
+        ops += ks[pos:pos + take]
         pos += take
         ops += pv[t]
-    ops += s_ops[pos:]
-    assert len(ops) == len(s_ops) + 16
-
-    # VALU stream: maximum, refresh test + branch, then exp of steps 0..3.
-    valu = [(x, w, -1) for x, w in max_items(cur)]
-    valu.append((rescale_block(), 6, -1))
+    assert pos == len(ks) and len(ops) == len(ks) + 16
+    exp_q = []
     for t in range(4):
         for qb in range(2):
-            valu += [(x, w, t) for x, w in exp_items(cur, qb, t)]
-    # done_at[t]: VALU items that must precede the first P.V MFMA of step t
-    done_at = {t: max(i for i, v in enumerate(valu) if v[2] == t) + 1 for t in range(4)}
-
-    lines = []
-    vi = 0          # next VALU item
-    since_p = {}    # instruction count since the last write of each P operand
-
-    def emit(text):
-        lines.append(text)
-        for k in since_p:
-            since_p[k] += 1
-
-    def emit_valu(n_weight):
-        nonlocal vi
-        w = 0
-        while vi < len(valu) and w < n_weight:
-            text, wt, t = valu[vi]
-            for ln in text.split("\n"):
-                emit(ln)
-            if text.startswith("v_cvt_pk_bf16_f32"):
-                since_p[text.split()[1].rstrip(",")] = 0
-            w += wt
-            vi += 1
-
-    n = len(ops)
-    slots = [i % NRING for i in range(n)]
-    issued = 0
-    for i in range(min(LOOKAHEAD, n)):
-        emit(read_text(ops[i], slots[i], kbuf, vbuf))
-        issued += 1
-    for i, op in enumerate(ops):
-        # VALU needed before this operand's MFMAs
-        if op.exp_t is not None:
-            need = done_at[op.exp_t]
-            if vi < need:
-                emit_valu(sum(v[1] for v in valu[vi:need]))
-            # the P operand registers: two instructions after their last write
-            for qb in range(2):
-                preg = f"v{sreg(cur, qb, op.exp_t >> 1, 8 * (op.exp_t & 1) + 3)}"
-                if preg in since_p and since_p[preg] < 2:
-                    emit("s_nop 1")
-        emit(f"s_waitcnt lgkmcnt({min(issued - 1 - i, 15)})")
-        texts = mfma_texts(op, slots[i], cur, nxt)
-        # VALU weight to place beside each MFMA: spread evenly up to the next deadline
-        nxt_t = next((o.exp_t for o in ops[i:] if o.exp_t is not None and vi < done_at[o.exp_t]), None)
-        if nxt_t is not None:
-            dl = next(j for j in range(i, n) if ops[j].exp_t == nxt_t)
-            mfmas = 2 * max(dl - i, 1)
-            rest = sum(v[1] for v in valu[vi:done_at[nxt_t]])
-            per = math.ceil(rest / mfmas)
-        else:
-            rest = sum(v[1] for v in valu[vi:])
-            per = math.ceil(rest / (2 * (n - i))) if rest else 0
-        for k, mt in enumerate(texts):
-            emit(mt)
-            if k == 0 and i + LOOKAHEAD < n:
-                j = i + LOOKAHEAD
-                emit(read_text(ops[j], slots[j], kbuf, vbuf))
-                issued += 1
-            emit_valu(per)
-    emit_valu(10 ** 9)
-    assert vi == len(valu)
-    return lines
+            exp_q += [(x, w, t) for x, w in exp_items(cur, qb, t)]
+    post_q, final, tail = [], [], []
+    if nxt is not None:
+        post_q = [(mask_block(nxt), 2)] + max_items(nxt)
+        final = refresh_block().split("\n")
+        # the previous tile's K/V DMA has landed (this tile's eight may be in
+        # flight) and every wave is done with the slots the next DMA refills
+        tail = ["s_waitcnt vmcnt(8)", "s_barrier"]
+    lines = addr_lines(k=nxt is not None)
+    return lines + schedule(ops, exp_q, post_q, final, cur, nxt, list(range(8)) if nxt is not None else [], tail)
 
 
-def scores_body(nxt, kbuf):
-    """Scores of a unit's first tile into set nxt (no softmax), then padding
-    so that the VALU reads of the next block see the finished MFMAs."""
-    ops = [Operand("K", kb, s) for s in range(8) for kb in range(2)]
+def scores_body(nxt):
+    """A unit's first tile: its scores into set nxt, masked, their maximum
+    and the first running-maximum refresh (no softmax yet)."""
+    post_q = [(mask_block(nxt), 2)] + max_items(nxt)
     lines = ["s_nop 3"]   # Q^T and O^T were just written to AGPRs
-    n = len(ops)
-    issued = 0
-    for i in range(LOOKAHEAD):
-        lines.append(read_text(ops[i], i % NRING, kbuf, 0))
-        issued += 1
-    for i, op in enumerate(ops):
-        lines.append(f"s_waitcnt lgkmcnt({min(issued - 1 - i, 15)})")
-        texts = mfma_texts(op, i % NRING, None, nxt)
-        for k, mt in enumerate(texts):
-            lines.append(mt)
-            if k == 0 and i + LOOKAHEAD < n:
-                j = i + LOOKAHEAD
-                lines.append(read_text(ops[j], j % NRING, kbuf, 0))
-                issued += 1
-    lines += ["s_nop 7", "s_nop 7", "s_nop 7"]
-    return lines
-
-
-def mask_body(cur):
-    """Scores of keys outside [lo_i, pos_i] of their query become -inf:
-    element (kb, e) of block qb holds key c + 8 half + tile start, visible iff
-    c - a_qb <= span_qb (unsigned), a_qb = lo_i - tile start - 8 half. Skipped
-    as a whole when the wave-uniform flag `full` is set (every key of the
-    tile visible to every row of the wave): a branch inside the block keeps
-    the caller free of control flow around the pinned registers."""
-    lines = ["s_cmp_lg_u32 %[full], 0",
-             "s_cbranch_scc1 .Lw2full_%=",
-             f"v_mov_b32 {T(8)}, {NEG_INF}"]
-    k = 0
-    for qb in range(2):
-        for kb in range(2):
-            for e in range(16):
-                t = T(9 + (k & 1))
-                r = f"v{sreg(cur, qb, kb, e)}"
-                lines += [f"v_sub_u32 {t}, {key_const(kb, e)}, %[a{qb}]",
-                          f"v_cmp_le_u32 vcc, {t}, %[s{qb}]",
-                          f"v_cndmask_b32 {r}, {T(8)}, {r}, vcc"]
-                k += 1
-    lines.append(".Lw2full_%=:")
-    return lines
+    lines += addr_lines(v=False)
+    return lines + schedule(s_ops(), [], post_q, refresh_block().split("\n"), None, nxt, [], [])
 
 
 CLOBBER = (", ".join(f'"v{i}"' for i in range(OWN, 256)) + ", " + ", ".join(f'"a{i}"' for i in range(OWN, 256)) +
-           ', "vcc", "scc", "memory"')
+           ', "vcc", "scc", "m0", "memory"')
 TILE_OUT = '[m0] "+v"(m0), [m1] "+v"(m1), [l0] "+v"(l0), [l1] "+v"(l1)'
-TILE_IN = ('[ka0] "v"(ad.ka[0]), [ka1] "v"(ad.ka[1]), [ka2] "v"(ad.ka[2]), [ka3] "v"(ad.ka[3]), '
+ADDR_IN = ('[ka0] "v"(ad.ka[0]), [ka1] "v"(ad.ka[1]), [ka2] "v"(ad.ka[2]), [ka3] "v"(ad.ka[3]), '
            '[ka4] "v"(ad.ka[4]), [ka5] "v"(ad.ka[5]), [ka6] "v"(ad.ka[6]), [ka7] "v"(ad.ka[7]), '
            '[va0] "v"(ad.va[0]), [va1] "v"(ad.va[1]), [va2] "v"(ad.va[2]), [va3] "v"(ad.va[3]), '
-           '[scale] "s"(scale)')
-TILE_PARAMS = "float &m0, float &m1, float &l0, float &l1, const W2Addr &ad, float scale"
+           '[scale] "s"(scale), [kslot] "s"(st.kslot), [vslot] "s"(st.vslot)')
+DMA_IN = ('[rk] "s"(st.rk), [rv] "s"(st.rv), [sok] "s"(st.sok), [sov] "s"(st.sov), [m0k] "s"(st.m0k), '
+          '[m0v] "s"(st.m0v), [kd0] "v"(ad.kd[0]), [kd1] "v"(ad.kd[1]), [kd2] "v"(ad.kd[2]), [kd3] "v"(ad.kd[3]), '
+          '[vd0] "v"(ad.vd[0]), [vd1] "v"(ad.vd[1]), [vd2] "v"(ad.vd[2]), [vd3] "v"(ad.vd[3])')
+MASK_IN = '[a0] "v"(mk.a0), [s0] "v"(mk.s0), [a1] "v"(mk.a1), [s1] "v"(mk.s1), [full] "s"(mk.full)'
+TILE_IN = ADDR_IN + ", " + DMA_IN + ", " + MASK_IN
+TILE_PARAMS = ("float &m0, float &m1, float &l0, float &l1, const W2Addr &ad, const W2Step &st, const W2Mask &mk, "
+               "float scale")
 
 
 def c_string(lines, indent="        "):
@@ -366,33 +446,26 @@ def generate():
     # O^T = 0
     parts.append(function("w2_zero_o", "O^T accumulators to zero.",
                           [f"v_accvgpr_write_b32 a{OA + i}, 0" for i in range(128)], "", "", ""))
-    # Q^T, one 16-byte chunk (k-step s of block qb) at a time
-    body = []
-    for qb in range(2):
-        for st in range(8):
-            a = QA + 32 * qb + 4 * st
-            lines = [f"v_accvgpr_write_b32 a{a + i}, %[x{i}]" for i in range(4)]
-            body.append(f"    {'if' if qb + st == 0 else 'else if'} constexpr (QB == {qb} && S == {st})\n"
-                        f"        asm volatile(\n{c_string(lines, '            ')}\n"
-                        f"            :\n            : [x0] \"v\"(x0), [x1] \"v\"(x1), [x2] \"v\"(x2), [x3] \"v\"(x3)\n"
-                        f"            : {CLOBBER});\n")
-    parts.append("// One 16-byte chunk of Q^T (block QB, k-step S) into its AGPRs.\n"
-                 "template <int QB, int S>\n"
-                 "__device__ __forceinline__ void w2_set_q(unsigned x0, unsigned x1, unsigned x2, unsigned x3)\n{\n" +
-                 "".join(body) + "}\n")
-    parts.append(function("w2_scores_first", "Scores of the first tile (K buffer 0) into set X.",
-                          scores_body(XB, 0), "", TILE_IN, "const W2Addr &ad, float scale"))
-    for name, cur, nxt, kbuf, vbuf in (("w2_tile_xy", XB, YB, 1, 0), ("w2_tile_yx", YB, XB, 0, 1)):
-        doc = (f"Tile with scores in set {'X' if cur == XB else 'Y'} (V^T buffer {vbuf}); next tile's "
-               f"scores into set {'Y' if nxt == YB else 'X'} from K buffer {kbuf}.")
-        parts.append(function(name, doc, tile_body(cur, nxt, kbuf, vbuf), TILE_OUT, TILE_IN, TILE_PARAMS))
-    for name, cur, vbuf in (("w2_last_x", XB, 0), ("w2_last_y", YB, 1)):
-        doc = f"A unit's last tile, scores in set {'X' if cur == XB else 'Y'} (V^T buffer {vbuf})."
-        parts.append(function(name, doc, tile_body(cur, None, 0, vbuf), TILE_OUT, TILE_IN, TILE_PARAMS))
-    mask_in = '[a0] "v"(a0), [s0] "v"(s0), [a1] "v"(a1), [s1] "v"(s1), [full] "s"(full)'
-    for name, cur in (("w2_mask_x", XB), ("w2_mask_y", YB)):
-        parts.append(function(name, f"Mask the scores in set {'X' if cur == XB else 'Y'}.", mask_body(cur), "",
-                              mask_in, "int a0, unsigned s0, int a1, unsigned s1, unsigned full"))
+    # Q^T straight from memory into its AGPRs: 16 loads in flight, no wait
+    # (the caller's barrier waits for them)
+    lines = [f"buffer_load_dwordx4 {ablk(QA + 32 * qb + 4 * st, 4)}, %[q{qb}], %[rq], 0 offen offset:{32 * st}"
+             for qb in range(2) for st in range(8)]
+    parts.append(function("w2_load_q", "Q^T of both blocks into its AGPRs: lane chunk s of block qb from "
+                          "byte offset q_qb + 32 s of the buffer rq (an offset past its end reads zeros).",
+                          lines, "", '[rq] "s"(rq), [q0] "v"(q0), [q1] "v"(q1)',
+                          "__amdgpu_buffer_rsrc_t rq, unsigned q0, unsigned q1"))
+    parts.append(function("w2_scores_first", "A unit's first tile (K slot st.kslot): scores into set X, masked, "
+                          "their maximum, the first running-maximum refresh.",
+                          scores_body(XB), TILE_OUT, ADDR_IN + ", " + MASK_IN, TILE_PARAMS))
+    for name, cur, nxt in (("w2_tile_xy", XB, YB), ("w2_tile_yx", YB, XB)):
+        doc = (f"Tile with scores in set {'X' if cur == XB else 'Y'}; next tile's scores into set "
+               f"{'Y' if nxt == YB else 'X'} (masked with mk, maximum, refresh); DMA of later tiles; wait + barrier.")
+        parts.append(function(name, doc, tile_body(cur, nxt), TILE_OUT, TILE_IN, TILE_PARAMS))
+    for name, cur in (("w2_last_x", XB), ("w2_last_y", YB)):
+        doc = f"A unit's last tile, scores in set {'X' if cur == XB else 'Y'} (no DMA, no barrier)."
+        parts.append(function(name, doc, tile_body(cur, None), TILE_OUT, ADDR_IN,
+                              "float &m0, float &m1, float &l0, float &l1, const W2Addr &ad, const W2Step &st, "
+                              "float scale"))
     parts.append(function("w2_drain", "Wait until the last MFMAs writing O^T have finished.",
                           ["s_nop 7", "s_nop 7", "s_nop 7"], "", "", ""))
     # O^T read-out: four consecutive accumulator registers of (block QB, dim block DB, group J)

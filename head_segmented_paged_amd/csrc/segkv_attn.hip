@@ -802,11 +802,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
 // and P.V work in a fixed interleave. The loop around them (page ids, K/V
 // DMA into LDS, barriers, masking decisions) is the pipelined kernel's, with
 // four waves.
-constexpr unsigned kW2Lds = 4 * 16384;   // dynamic LDS of the two-block kernel: two K and two V^T tiles
+// Dynamic LDS of the two-block kernel: a three-slot ring of K tiles, then a
+// three-slot ring of V^T tiles.
+constexpr unsigned kW2Slot = 16384;
+constexpr unsigned kW2VRing = 3 * kW2Slot;
+constexpr unsigned kW2Lds = 6 * kW2Slot;
 
 struct W2Addr {
-    unsigned ka[8];          // K operand of k-step s, K buffer 0 (LDS byte address)
-    unsigned va[4];          // V^T operand of 16-key step t, V buffer 0
+    unsigned ka[8];          // K operand of k-step s: LDS byte offset within a K slot (lane's row and chunk)
+    unsigned va[4];          // V^T operand of 16-key step t: LDS address within V slot 0
+    unsigned kd[4], vd[4];   // the lane's DMA source offsets within a K / V page (bytes)
+};
+// Per-tile scalars of the tile bodies (wave-uniform).
+struct W2Step {
+    __amdgpu_buffer_rsrc_t rk, rv;   // source pages of the K tile three ahead and the V^T tile two ahead
+    unsigned sok, sov;               // their first key's byte offset within the page
+    unsigned m0k, m0v;               // LDS destination of this wave's DMA instructions
+    unsigned kslot, vslot;           // LDS address of the K slot read now, offset of the V^T slot read now
+};
+// Masking of a tile's scores (lane-varying bounds, wave-uniform skip flag).
+struct W2Mask {
+    int a0, a1;                      // lo_i - tile start - 8 half, per block
+    unsigned s0, s1;                 // pos_i - lo_i, per block
+    unsigned full;                   // every key of the tile visible to every row of the wave
 };
 
 // The blocks clobber registers above the kernel's own budget on purpose (that
@@ -827,15 +845,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     constexpr int D = 128, NW = 4;
     using T = DmaTile<D, NW>;
     constexpr int kUnitRows = 256 / HPW;       // rows per unit (eight 32-row blocks over HPW heads)
-    constexpr int kBuf = 16384;                // one K or V^T tile
-    static_assert(T::kBytes == kBuf && T::vBytes == kBuf, "tile bodies assume 16 KB tiles");
-    // K buffers 0, 1 then V^T buffers 0, 1 (4 kBuf bytes of dynamic LDS): the
-    // tile bodies address buffer 1 as buffer 0 plus kBuf. The LDS is dynamic
-    // so that the compiler's occupancy estimate does not raise the kernel's
-    // own register budget into the range the tile bodies keep their state in.
+    static_assert(T::kBytes == kW2Slot && T::vBytes == kW2Slot, "tile bodies assume 16 KB tiles");
+    // kW2Lds bytes of dynamic LDS: the K ring, then the V^T ring. The LDS is
+    // dynamic so that the compiler's occupancy estimate does not raise the
+    // kernel's own register budget into the range the tile bodies keep their
+    // state in.
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    char *const kbuf0 = smem, *const kbuf1 = smem + kBuf, *const vbuf0 = smem + 2 * kBuf,
-               *const vbuf1 = smem + 3 * kBuf;
 
     const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
@@ -895,80 +910,91 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     }
     const int wp_lo = q_pos0 + wr_first, wp_hi = q_pos0 + wr_last;
 
-    // Q^T of both blocks into its AGPRs, one 16-byte chunk at a time; O^T = 0.
-    auto set_q = [&](auto qb_c) {
-        constexpr int k = decltype(qb_c)::value;
-        const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
-        const u16 *qp = q + (my_row[k] * hq + min(head[k], hq - 1)) * D + 8 * half;
-        auto chunk = [&](auto s_c) {
-            constexpr int s = decltype(s_c)::value;
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (can_load) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
-            w2_set_q<k, s>(raw[0], raw[1], raw[2], raw[3]);
-        };
-        chunk(std::integral_constant<int, 0>{});
-        chunk(std::integral_constant<int, 1>{});
-        chunk(std::integral_constant<int, 2>{});
-        chunk(std::integral_constant<int, 3>{});
-        chunk(std::integral_constant<int, 4>{});
-        chunk(std::integral_constant<int, 5>{});
-        chunk(std::integral_constant<int, 6>{});
-        chunk(std::integral_constant<int, 7>{});
-    };
-    set_q(std::integral_constant<int, 0>{});
-    set_q(std::integral_constant<int, 1>{});
+    // Q^T of both blocks into its AGPRs (issued now, waited for by the
+    // prologue's barrier): a buffer over the unit's rows of Q, so a lane
+    // whose row or head does not exist reads zeros.
+    {
+        const int64_t urow0 = static_cast<int64_t>(q_row0) + row0;   // first Q row of the unit
+        const int64_t urows = max<int64_t>(0, min<int64_t>(unit_end - row0, total_q_rows - urow0));
+        const __amdgpu_buffer_rsrc_t rq =
+            page_rsrc(q + urow0 * hq * D, static_cast<int>(urows * hq * D * 2));
+        unsigned qo[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
+            qo[k] = can_load ? static_cast<unsigned>(((my_row[k] - urow0) * hq + head[k]) * D * 2 + 16 * half)
+                             : 0x80000000u;
+        }
+        w2_load_q(rq, qo[0], qo[1]);
+    }
     w2_zero_o();
     float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;   // running maximum (log2 domain) and sum per block
 
-    int win = ((tile_beg * kBK) >> log2P) >> 6;
-    auto load_window = [&](int w) { return pages[min(w * 64 + lane, n_pages - 1)]; };
-    int win_cur = load_window(win), win_next = load_window(win + 1);
-    auto tile_page = [&](int jt) {
-        const int lp = (jt * kBK) >> log2P;
-        if ((lp >> 6) != win) {
-            win = lp >> 6;
-            win_cur = win_next;
-            win_next = load_window(win + 1);
-        }
-        const int id = __builtin_amdgcn_readlane(win_cur, lp & 63);
-        return (lp < n_pages && id >= 0 && id < num_pages) ? id : -1;
+    // Page id of tile jt (or -1): one scalar load from the segment's page
+    // list. Scalar loads keep the vector-memory counter, which the tile
+    // bodies' DMA uses, free of the compiler's own waits.
+    // The id is checked when its buffer resource is built, a body later.
+    auto page_at = [&](int jt) {
+        const int lp = __builtin_amdgcn_readfirstlane((jt * kBK) >> log2P);
+        if (lp < 0 || lp >= n_pages) return -1;
+        return __builtin_amdgcn_readfirstlane(pages[lp]);
     };
 
-    unsigned kdma[T::kInstr], vdma[T::vInstr];
+    const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem));
+    W2Addr ad;
 #pragma unroll
     for (int i = 0; i < T::kInstr; ++i) {
         const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
         const int rr = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(rr);
-        kdma[i] = static_cast<unsigned>(rr * T::kRowBytes + c * 16);
+        ad.kd[i] = static_cast<unsigned>(rr * T::kRowBytes + c * 16);
     }
 #pragma unroll
     for (int i = 0; i < T::vInstr; ++i) {
         const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
         const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
-        vdma[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
+        ad.vd[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
     }
-    auto dma_k = [&](char *dst, int page, int jt) {
-        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
-        const int64_t pg = page >= 0 ? page : 0;
-        const __amdgpu_buffer_rsrc_t rk =
-            page_rsrc(kpool + ((pg * D) << log2P), page >= 0 ? (T::kRowBytes << log2P) : 0);
+    {
+        const int krow = swizzle_row(col);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            ad.ka[s] = static_cast<unsigned>(krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            ad.va[t] = lds0 + kW2VRing + static_cast<unsigned>(col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
+    }
+    // Buffer resource of a tile's page (a missing page, or a tile past the
+    // unit's run, has no records: its DMA reads zeros) and the byte offset of
+    // the tile's first key in that page.
+    auto k_rsrc = [&](int page) {
+        const bool ok = page >= 0 && page < num_pages;
+        const int64_t pg = ok ? page : 0;
+        return page_rsrc(kpool + ((pg * D) << log2P), ok ? (T::kRowBytes << log2P) : 0);
+    };
+    auto v_rsrc = [&](int page) {
+        const bool ok = page >= 0 && page < num_pages;
+        const int64_t pg = ok ? page : 0;
+        return page_rsrc(vpool + ((pg * D) << log2P), ok ? ((D * 2) << log2P) : 0);
+    };
+    auto slot0 = [&](int jt) { return static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1)); };
+    auto dma_k = [&](unsigned slot, int page, int jt) {
+        const __amdgpu_buffer_rsrc_t rk = k_rsrc(page);
 #pragma unroll
         for (int i = 0; i < T::kInstr; ++i)
-            dma16(rk, dst + (wave * T::kInstr + i) * 1024, kdma[i], slot0 * T::kRowBytes);
+            dma16(rk, smem + slot * kW2Slot + (wave * T::kInstr + i) * 1024, ad.kd[i], slot0(jt) * T::kRowBytes);
     };
-    auto dma_v = [&](char *dst, int page, int jt) {
-        const unsigned slot0 = static_cast<unsigned>((jt * kBK) & ((1 << log2P) - 1));
-        const int64_t pg = page >= 0 ? page : 0;
-        const __amdgpu_buffer_rsrc_t rv = page_rsrc(vpool + ((pg * D) << log2P), page >= 0 ? ((D * 2) << log2P) : 0);
+    auto dma_v = [&](unsigned slot, int page, int jt) {
+        const __amdgpu_buffer_rsrc_t rv = v_rsrc(page);
 #pragma unroll
         for (int i = 0; i < T::vInstr; ++i)
-            dma16(rv, dst + (wave * T::vInstr + i) * 1024, vdma[i], slot0 * 2);
+            dma16(rv, smem + kW2VRing + slot * kW2Slot + (wave * T::vInstr + i) * 1024, ad.vd[i], slot0(jt) * 2);
     };
     auto edge_tile = [&](int jt) {
         const int key0 = jt * kBK;
         return key0 < zero_lo || key0 + kBK > zero_hi;
     };
-    auto fixup = [&](char *vb, int jt) {
+    auto fixup = [&](unsigned slot, int jt) {
+        char *vb = smem + kW2VRing + slot * kW2Slot;
         const int key0 = jt * kBK;
         for (int e = threadIdx.x; e < D * kBK; e += NW * 64) {
             const int d = e / kBK, k = e % kBK, idx = key0 + k;
@@ -976,21 +1002,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
                 *reinterpret_cast<u16 *>(vb + d * 128 + (((k >> 3) ^ vswz(d)) << 4) + (k & 7) * 2) = 0;
         }
     };
-
-    // LDS operand addresses (buffer 0; the tile bodies add the buffer and
-    // 32-row block offsets as instruction offsets).
-    W2Addr ad;
-    {
-        const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem));
-        const int krow = swizzle_row(col);
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            ad.ka[s] = base + static_cast<unsigned>(krow * T::kRowBytes + (((2 * s + half) ^ kswz<D>(krow)) << 4));
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            ad.va[t] = base + 2 * kBuf + static_cast<unsigned>(col * 128 + (((2 * t + half) ^ vswz(col)) << 4));
-    }
-
     auto tile_full = [&](int jt) {
         const int kp0 = k_pos0 + jt * kBK;
         return (kp0 + kBK - 1 <= wp_lo) && (window == 0 || kp0 >= wp_hi - window + 1);
@@ -1001,72 +1012,94 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         a = lo_i[k] - kbase;
         s = static_cast<unsigned>(my_pos[k] - lo_i[k]);
     };
-    auto mask_x = [&](int jt) {
-        int a0, a1;
-        unsigned s0, s1;
-        mask_args(jt, 0, a0, s0);
-        mask_args(jt, 1, a1, s1);
-        w2_mask_x(a0, s0, a1, s1, __builtin_amdgcn_readfirstlane(tile_full(jt) ? 1u : 0u));
-    };
-    auto mask_y = [&](int jt) {
-        int a0, a1;
-        unsigned s0, s1;
-        mask_args(jt, 0, a0, s0);
-        mask_args(jt, 1, a1, s1);
-        w2_mask_y(a0, s0, a1, s1, __builtin_amdgcn_readfirstlane(tile_full(jt) ? 1u : 0u));
+    auto mask = [&](int jt) {
+        W2Mask mk;
+        mask_args(jt, 0, mk.a0, mk.s0);
+        mask_args(jt, 1, mk.a1, mk.s1);
+        mk.full = __builtin_amdgcn_readfirstlane(tile_full(jt) ? 1u : 0u);
+        return mk;
     };
 
-    // Iteration jt, parity A: scores of jt in X, next into Y from K buffer 1,
-    // V^T(jt) in buffer 0; meanwhile V(jt+1) is DMA'd into V buffer 1 and
-    // K(jt+2) into K buffer 0. Parity B mirrors it. A unit's last tile runs
-    // the variant without next scores.
+    // Ring: tile jt's K tile sits in K slot (jt - tile_beg) % 3 and its V^T
+    // tile in V slot (jt - tile_beg) % 3. The body of tile jt reads K(jt+1)
+    // and V(jt), and issues the DMA of K(jt+3) and V(jt+2), whose slots held
+    // K(jt) and V(jt-1), read by the previous body (before its barrier).
     if (tile_beg < tile_end) {
-        int page_v = -1;   // page of tile jt + 1, looked up when its K was fetched
-        const int page0 = tile_page(tile_beg);
-        dma_k(kbuf0, page0, tile_beg);
-        dma_v(vbuf0, page0, tile_beg);
-        if (tile_beg + 1 < tile_end) {
-            page_v = tile_page(tile_beg + 1);
-            dma_k(kbuf1, page_v, tile_beg + 1);
-        }
+        int pg[4];   // pages of tiles jt .. jt+3 at the top of the loop
+        pg[0] = page_at(tile_beg);
+        pg[1] = tile_beg + 1 < tile_end ? page_at(tile_beg + 1) : -1;
+        pg[2] = tile_beg + 2 < tile_end ? page_at(tile_beg + 2) : -1;
+        pg[3] = tile_beg + 3 < tile_end ? page_at(tile_beg + 3) : -1;
+        dma_k(0, pg[0], tile_beg);
+        dma_v(0, pg[0], tile_beg);
+        dma_k(1, pg[1], tile_beg + 1);
+        dma_v(1, pg[1], tile_beg + 1);
+        dma_k(2, pg[2], tile_beg + 2);
         __syncthreads();
-        if (edge_tile(tile_beg)) fixup(vbuf0, tile_beg);
-        w2_scores_first(ad, scale_log2);
-        __syncthreads();   // kbuf0 is refilled by the first iteration; the V fixup is visible
+        if (edge_tile(tile_beg)) fixup(0, tile_beg);   // V(jt+1) is fixed after body jt's barrier
+        W2Step st;
+        st.kslot = lds0;
+        st.vslot = 0;
+        w2_scores_first(m0, m1, l0, l1, ad, st, mask(tile_beg), scale_log2);
+        __syncthreads();   // K slot 0 is refilled by the first body; the fixups are visible
+        unsigned sk = 0;   // K slot of tile jt (= slot of tile jt+3); V slot of jt is sk as well
+        auto step = [&](int jt) {
+            // scalars of the body of tile jt; the page of tile jt+4 is loaded
+            // now and used a body later
+            const unsigned sk1 = sk == 2 ? 0 : sk + 1, sk2 = sk1 == 2 ? 0 : sk1 + 1;
+            const int pk = pg[3];
+            W2Step s;
+            s.rk = k_rsrc(pk);
+            s.rv = v_rsrc(pg[2]);
+            s.sok = slot0(jt + 3) * T::kRowBytes;
+            s.sov = slot0(jt + 2) * 2;
+            s.m0k = lds0 + sk * kW2Slot + wave * T::kInstr * 1024;
+            s.m0v = lds0 + kW2VRing + sk2 * kW2Slot + wave * T::vInstr * 1024;
+            s.kslot = lds0 + sk1 * kW2Slot;
+            s.vslot = sk * kW2Slot;
+            pg[0] = pg[1];
+            pg[1] = pg[2];
+            pg[2] = pk;
+            // The next page id is requested only after everything above has
+            // consumed the older ones: scalar loads complete out of order, so
+            // a use of an older id waits for every load in flight.
+            asm volatile("" ::"s"(s.rk), "s"(s.rv), "s"(pg[1]), "s"(pg[2]) : "memory");
+            pg[3] = jt + 4 < tile_end ? page_at(jt + 4) : -1;
+            sk = sk1;
+            return s;
+        };
         for (int jt = tile_beg;; jt += 2) {
             if (jt + 1 >= tile_end) {
-                mask_x(jt);
-                w2_last_x(m0, m1, l0, l1, ad, scale_log2);
+                W2Step s;
+                s.kslot = lds0;
+                s.vslot = sk * kW2Slot;
+                w2_last_x(m0, m1, l0, l1, ad, s, scale_log2);
                 break;
             }
-            dma_v(vbuf1, page_v, jt + 1);
-            if (jt + 2 < tile_end) {
-                page_v = tile_page(jt + 2);
-                dma_k(kbuf0, page_v, jt + 2);
-            }
-            mask_x(jt);
-            w2_tile_xy(m0, m1, l0, l1, ad, scale_log2);
-            __syncthreads();
-            if (edge_tile(jt + 1)) {
-                fixup(vbuf1, jt + 1);
-                __syncthreads();
+            {
+                const unsigned vs1 = sk == 2 ? 0 : sk + 1;   // V slot of tile jt+1
+                const W2Step s = step(jt);
+                w2_tile_xy(m0, m1, l0, l1, ad, s, mask(jt + 1), scale_log2);
+                if (edge_tile(jt + 1)) {
+                    fixup(vs1, jt + 1);
+                    __syncthreads();
+                }
             }
             if (jt + 2 >= tile_end) {
-                mask_y(jt + 1);
-                w2_last_y(m0, m1, l0, l1, ad, scale_log2);
+                W2Step s;
+                s.kslot = lds0;
+                s.vslot = sk * kW2Slot;
+                w2_last_y(m0, m1, l0, l1, ad, s, scale_log2);
                 break;
             }
-            dma_v(vbuf0, page_v, jt + 2);
-            if (jt + 3 < tile_end) {
-                page_v = tile_page(jt + 3);
-                dma_k(kbuf1, page_v, jt + 3);
-            }
-            mask_y(jt + 1);
-            w2_tile_yx(m0, m1, l0, l1, ad, scale_log2);
-            __syncthreads();
-            if (edge_tile(jt + 2)) {
-                fixup(vbuf0, jt + 2);
-                __syncthreads();
+            {
+                const unsigned vs1 = sk == 2 ? 0 : sk + 1;   // V slot of tile jt+2
+                const W2Step s = step(jt + 1);
+                w2_tile_yx(m0, m1, l0, l1, ad, s, mask(jt + 2), scale_log2);
+                if (edge_tile(jt + 2)) {
+                    fixup(vs1, jt + 2);
+                    __syncthreads();
+                }
             }
         }
     }
@@ -1738,12 +1771,17 @@ int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, vo
         // decode units take any G heads; every prefill kernel is built per heads-per-unit
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: unsupported unit_heads %d", t.unit_heads);
     } else if (big_page && t.unit_rows * t.unit_heads == kWideWaves * kWaveRows) {
-        if constexpr (D == 128)
+        if constexpr (D == 128) {
+            // 96 KB of dynamic LDS: above the default limit, set per launch (the
+            // attribute is per device)
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_prefill_w2_kernel<HPW, OUT_BF16>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kW2Lds);
+            if (e != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: LDS attribute: %s", hipGetErrorString(e));
             hipLaunchKernelGGL((attn_prefill_w2_kernel<HPW, OUT_BF16>), grid, dim3(4 * 64), kW2Lds, stream, qh, kp, vp,
                                cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
                                t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts,
                                t.num_parts);
-        else
+        } else
             hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWideWaves>), grid, dim3(kWideWaves * 64),
                                0, stream, qh, kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list,
                                t.num_page_entries, t.work, t.num_segments, t.total_q_rows, cfg.num_q_heads,
