@@ -120,13 +120,15 @@ class Operand:
         return self.b if self.kind == "V" else None
 
 
-def read_text(op, slot):
+def read_text(op, slot, koff=0, voff=0):
+    """LDS read of operand op into ring slot `slot`; koff / voff: byte offset
+    of the K / V^T ring slot from the address registers."""
     r = RING0 + 4 * slot
     if op.kind == "K":
         kb, s = op.a, op.b
-        return f"ds_read_b128 {vblk(r, 4)}, v{KADDR + s} offset:{kb * KB_BYTES}"
+        return f"ds_read_b128 {vblk(r, 4)}, v{KADDR + s} offset:{koff + kb * KB_BYTES}"
     db, t = op.a, op.b
-    return f"ds_read_b128 {vblk(r, 4)}, v{VADDR + t} offset:{db * DB_BYTES}"
+    return f"ds_read_b128 {vblk(r, 4)}, v{VADDR + t} offset:{voff + db * DB_BYTES}"
 
 
 def addr_lines(k=True, v=True):
@@ -265,15 +267,16 @@ def exp_items(s_set, qb, t):
     return order
 
 
-def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail):
+def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail, head=(), koff=0, voff=0):
     """Interleave the MFMA operand stream `ops` with
       exp_q:  (text, weight, t) items, all of step t due before its first P.V MFMA;
       post_q: (text, weight) items that read the scores of the next tile, so
               only once every S MFMA of the body is HAZ_MFMA_VALU instructions
               old;
       final:  lines after the last MFMA and the queues (the refresh);
-    plus the LDS operand reads (LOOKAHEAD operands ahead), the DMA
-    instructions after the MFMAs listed in DMA_AFTER, and `tail`. Beside each
+    plus the LDS operand reads (LOOKAHEAD operands ahead; `head` goes right
+    after the first of them), the DMA line groups `dma` after the MFMAs listed
+    in DMA_AFTER, and `tail`. Beside each
     MFMA goes an even share of the remaining VALU weight, exponentials first
     whenever their deadline needs them."""
     lines = []
@@ -312,8 +315,9 @@ def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail):
 
     issued = 0
     for i in range(min(LOOKAHEAD, n)):
-        lines.append(read_text(ops[i], slots[i]))
+        lines.append(read_text(ops[i], slots[i], koff, voff))
         issued += 1
+    lines.extend(head)
     for i, op in enumerate(ops):
         if op.exp_t is not None:
             while ei < done_at.get(op.exp_t, 0):
@@ -329,12 +333,12 @@ def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail):
             mfma_no += 1
             if k == 0 and i + LOOKAHEAD < n:
                 j = i + LOOKAHEAD
-                lines.append(read_text(ops[j], slots[j]))
+                lines.append(read_text(ops[j], slots[j], koff, voff))
                 issued += 1
             if k == 1 and i == last_s:
                 s_end_at = len(lines)
             if pending_dma and mfma_no - 1 >= DMA_AFTER[len(dma) - len(pending_dma)]:
-                lines.extend(dma_lines(pending_dma.pop(0)))
+                lines.extend(pending_dma.pop(0))
             # this slot's share
             left = 2 * n - mfma_no + 1
             rest_exp = sum(v[1] for v in exp_q[ei:])
@@ -400,7 +404,8 @@ def tile_body(cur, nxt):
         # flight) and every wave is done with the slots the next DMA refills
         tail = ["s_waitcnt vmcnt(8)", "s_barrier"]
     lines = addr_lines(k=nxt is not None)
-    return lines + schedule(ops, exp_q, post_q, final, cur, nxt, list(range(8)) if nxt is not None else [], tail)
+    dma = [dma_lines(i) for i in range(8)] if nxt is not None else []
+    return lines + schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail)
 
 
 def scores_body(nxt):
@@ -410,6 +415,130 @@ def scores_body(nxt):
     lines = ["s_nop 3"]   # Q^T and O^T were just written to AGPRs
     lines += addr_lines(v=False)
     return lines + schedule(s_ops(), [], post_q, refresh_block().split("\n"), None, nxt, [], [])
+
+
+# Steady-state run (w2_run): six tile bodies unrolled, one per phase of the
+# three-slot ring and the two score sets, in one hardware loop. Only tiles
+# every row of the unit sees whole run here (no mask, no V^T fix-up), and the
+# per-tile scalars are computed inside the bodies, among the MFMAs:
+#   s[88:91]  K buffer resource (tile j+3), s[92:95] V^T resource (tile j+2)
+#   s84 / s83 their byte offsets within the page, s81 the pool's page count
+#   (capped at 2^31 - 1), s80 a temporary, s82 the page id of tile j+4
+#   (scalar load, waited for at the body's end).
+RUN_SGPRS = [f"s{i}" for i in range(80, 96)]
+KQ, VQ = "s[88:91]", "s[92:95]"
+RSRC_WORD3 = "0x20000"
+
+
+def run_dma(u):
+    """The eight DMA groups of run body u (K tile into K slot u % 3, V^T tile
+    into V slot (u + 2) % 3), each with one scalar instruction of the next
+    page-id load or the loop count between the M0 write and the DMA."""
+    fill = ["s_add_u32 s80, %[kk], 64",           # first key of tile j+4
+            "s_lshr_b32 s80, s80, %[log2p]",       # its page-list index
+            "s_min_u32 s80, s80, %[lastlp]",
+            "s_lshl_b32 s80, s80, 2",
+            "s_load_dword s82, %[pages], s80",
+            "s_add_u32 %[kk], %[kk], 64",
+            "s_sub_u32 %[cnt], %[cnt], 1",
+            "s_nop 0"]
+    groups = []
+    for i in range(4):
+        groups.append([f"s_add_u32 m0, %[m0k], {(u % 3) * 16384 + i * 1024}", fill[i],
+                       f"buffer_load_dwordx4 %[kd{i}], {KQ}, s84 offen lds"])
+    for i in range(4):
+        groups.append([f"s_add_u32 m0, %[m0v], {((u + 2) % 3) * 16384 + i * 1024}", fill[4 + i],
+                       f"buffer_load_dwordx4 %[vd{i}], {VQ}, s83 offen lds"])
+    return groups
+
+
+def run_body(u):
+    """Run body u: the tile whose position in the unit is u mod 6."""
+    cur, nxt = (XB, YB) if u % 2 == 0 else (YB, XB)
+    ks = s_ops()
+    pv = [[Operand("V", db, t) for db in range(4)] for t in range(4)]
+    ops, pos = [], 0
+    for t in range(4):
+        ops += ks[pos:pos + S_SPLIT[t]]
+        pos += S_SPLIT[t]
+        ops += pv[t]
+    exp_q = []
+    for t in range(4):
+        for qb in range(2):
+            exp_q += [(x, w, t) for x, w in exp_items(cur, qb, t)]
+    # K resource of tile j+3 and its offset in the page, before the first DMA
+    head = ["s_mul_i32 s88, %[idk], %[pbytes]",
+            "s_mul_hi_u32 s89, %[idk], %[pbytes]",
+            "s_add_u32 s88, s88, %[kplo]",
+            "s_addc_u32 s89, s89, %[kphi]",
+            "s_cmp_lt_u32 %[idk], s81",
+            "s_cselect_b32 s90, %[pbytes], 0",
+            "s_and_b32 s84, %[kk], %[pmask]",
+            "s_lshl_b32 s84, s84, 8"]
+    final = [f"v_sub_f32 {T(6)}, {T(4)}, %[m0]",
+             f"v_sub_f32 {T(7)}, {T(5)}, %[m1]",
+             f"v_max_f32 {T(6)}, {T(6)}, {T(7)}",
+             f"v_cmp_lt_f32 vcc, {SLACK_LOG2}, {T(6)}",
+             f"s_cbranch_vccnz .Lw2r{u}_%=",
+             f".Lw2k{u}_%=:"]
+    # next body's ids and V^T resource (this tile's K resource, moved to the
+    # V^T pool), then the usual wait + barrier, and the exit test
+    tail = ["s_waitcnt lgkmcnt(0)",
+            "s_mov_b32 %[idv], %[idk]",
+            "s_mov_b32 %[idk], s82",
+            "s_add_u32 s92, s88, %[vdlo]",
+            "s_addc_u32 s93, s89, %[vdhi]",
+            "s_mov_b32 s94, s90",
+            "s_lshr_b32 s83, s84, 7",
+            "s_cmp_eq_u32 %[cnt], 0",
+            "s_waitcnt vmcnt(8)",
+            "s_barrier",
+            "s_cbranch_scc1 .Lw2end_%="]
+    lines = [f".Lw2b{u}_%=:"]
+    return lines + schedule(ops, exp_q, max_items(nxt), final, cur, nxt, run_dma(u), tail, head=head,
+                            koff=((u + 1) % 3) * 16384, voff=(u % 3) * 16384)
+
+
+def run_block():
+    lines = [f"v_add_u32 v{KADDR + s}, %[kbase], %[ka{s}]" for s in range(8)]
+    lines += [f"v_mov_b32 v{VADDR + t}, %[va{t}]" for t in range(4)]
+    lines += ["s_mov_b64 s[80:81], %[npg]",
+              "s_cmp_lg_u32 s81, 0",
+              "s_cselect_b32 s80, 0x7fffffff, s80",
+              "s_min_u32 s81, s80, 0x7fffffff",
+              f"s_mov_b32 s91, {RSRC_WORD3}",
+              f"s_mov_b32 s95, {RSRC_WORD3}",
+              # V^T resource of tile j+2 and its offset in the page
+              "s_mul_i32 s92, %[idv], %[pbytes]",
+              "s_mul_hi_u32 s93, %[idv], %[pbytes]",
+              "s_add_u32 s92, s92, %[kplo]",
+              "s_addc_u32 s93, s93, %[kphi]",
+              "s_add_u32 s92, s92, %[vdlo]",
+              "s_addc_u32 s93, s93, %[vdhi]",
+              "s_cmp_lt_u32 %[idv], s81",
+              "s_cselect_b32 s94, %[pbytes], 0",
+              "s_sub_u32 s83, %[kk], 64",
+              "s_and_b32 s83, s83, %[pmask]",
+              "s_lshl_b32 s83, s83, 1"]
+    for u in range(1, 6):
+        lines += [f"s_cmp_eq_u32 %[ph], {u}", f"s_cbranch_scc1 .Lw2b{u}_%="]
+    for u in range(6):
+        lines += run_body(u)
+    lines.append("s_branch .Lw2b0_%=")
+    # running-maximum refresh, out of line, shared by the six bodies
+    for u in range(6):
+        lines += [f".Lw2r{u}_%=:", f"s_mov_b32 s80, {u}", "s_branch .Lw2ref_%="]
+    ref = refresh_block().split("\n")
+    # drop the in-line form's test and skip label: the bodies did the test
+    start = ref.index("s_cbranch_vccz .Lw2keep_%=")
+    ref = ref[start + 1:-1]
+    lines.append(".Lw2ref_%=:")
+    lines += ref
+    for u in range(5):
+        lines += [f"s_cmp_eq_u32 s80, {u}", f"s_cbranch_scc1 .Lw2k{u}_%="]
+    lines.append("s_branch .Lw2k5_%=")
+    lines.append(".Lw2end_%=:")
+    return lines
 
 
 CLOBBER = (", ".join(f'"v{i}"' for i in range(OWN, 256)) + ", " + ", ".join(f'"a{i}"' for i in range(OWN, 256)) +
@@ -461,6 +590,24 @@ def generate():
         doc = (f"Tile with scores in set {'X' if cur == XB else 'Y'}; next tile's scores into set "
                f"{'Y' if nxt == YB else 'X'} (masked with mk, maximum, refresh); DMA of later tiles; wait + barrier.")
         parts.append(function(name, doc, tile_body(cur, nxt), TILE_OUT, TILE_IN, TILE_PARAMS))
+    run_out = TILE_OUT + ', [cnt] "+s"(cnt), [kk] "+s"(kk), [idk] "+s"(idk), [idv] "+s"(idv)'
+    run_in = ('[ka0] "v"(ad.ka[0]), [ka1] "v"(ad.ka[1]), [ka2] "v"(ad.ka[2]), [ka3] "v"(ad.ka[3]), '
+              '[ka4] "v"(ad.ka[4]), [ka5] "v"(ad.ka[5]), [ka6] "v"(ad.ka[6]), [ka7] "v"(ad.ka[7]), '
+              '[va0] "v"(ad.va[0]), [va1] "v"(ad.va[1]), [va2] "v"(ad.va[2]), [va3] "v"(ad.va[3]), '
+              '[kd0] "v"(ad.kd[0]), [kd1] "v"(ad.kd[1]), [kd2] "v"(ad.kd[2]), [kd3] "v"(ad.kd[3]), '
+              '[vd0] "v"(ad.vd[0]), [vd1] "v"(ad.vd[1]), [vd2] "v"(ad.vd[2]), [vd3] "v"(ad.vd[3]), '
+              '[scale] "s"(scale), [kbase] "s"(rn.kbase), [m0k] "s"(rn.m0k), [m0v] "s"(rn.m0v), '
+              '[pages] "s"(rn.pages), [kplo] "s"(rn.kplo), [kphi] "s"(rn.kphi), [vdlo] "s"(rn.vdlo), '
+              '[vdhi] "s"(rn.vdhi), [pbytes] "s"(rn.pbytes), [npg] "s"(rn.npg), [lastlp] "s"(rn.lastlp), '
+              '[log2p] "s"(rn.log2p), [pmask] "s"(rn.pmask), [ph] "s"(phase)')
+    run_clob = CLOBBER + ", " + ", ".join(f'"{r}"' for r in RUN_SGPRS)
+    parts.append(function("w2_run", "Run of cnt tile bodies over tiles every row of the unit sees whole, entered "
+                          "at ring phase `phase` (tile position in the unit mod 6); kk = first key of tile j+3 "
+                          "within the segment, idk / idv = page ids of tiles j+3 / j+2 (all updated on exit).",
+                          run_block(), run_out, run_in,
+                          "float &m0, float &m1, float &l0, float &l1, const W2Addr &ad, const W2Run &rn, "
+                          "unsigned phase, unsigned &cnt, unsigned &kk, int &idk, int &idv, float scale",
+                          clobbers=run_clob))
     for name, cur in (("w2_last_x", XB), ("w2_last_y", YB)):
         doc = f"A unit's last tile, scores in set {'X' if cur == XB else 'Y'} (no DMA, no barrier)."
         parts.append(function(name, doc, tile_body(cur, None), TILE_OUT, ADDR_IN,

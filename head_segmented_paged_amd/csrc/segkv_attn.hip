@@ -820,6 +820,18 @@ struct W2Step {
     unsigned m0k, m0v;               // LDS destination of this wave's DMA instructions
     unsigned kslot, vslot;           // LDS address of the K slot read now, offset of the V^T slot read now
 };
+// Scalars of a steady-state run (w2_run), fixed for the unit.
+struct W2Run {
+    unsigned kbase;                  // LDS address of the rings
+    unsigned m0k, m0v;               // this wave's DMA destination in K slot 0 / V^T slot 0
+    const int32_t *pages;            // the segment's page list
+    unsigned kplo, kphi;             // K pool address
+    unsigned vdlo, vdhi;             // V^T pool address minus K pool address (mod 2^64)
+    unsigned pbytes;                 // bytes of one page of K (and of V^T)
+    int64_t npg;                     // pages in the pool (ids outside [0, npg) are not pages)
+    unsigned lastlp;                 // the segment's last page-list index
+    unsigned log2p, pmask;           // log2 of the page size, page size - 1
+};
 // Masking of a tile's scores (lane-varying bounds, wave-uniform skip flag).
 struct W2Mask {
     int a0, a1;                      // lo_i - tile start - 8 half, per block
@@ -1068,39 +1080,67 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
             sk = sk1;
             return s;
         };
-        for (int jt = tile_beg;; jt += 2) {
+        // Bodies jt whose next tile every row of the unit sees whole (no mask,
+        // no V^T fix-up) and whose DMA stays inside the unit's run go through
+        // w2_run: jt in [run_lo, run_hi).
+        auto floor_div = [](int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+        int64_t full_lo = -floor_div(-static_cast<int64_t>(zero_lo), kBK);   // first key at or above zero_lo
+        if (window) full_lo = max(full_lo, -floor_div(-(static_cast<int64_t>(last_pos) - window + 1 - k_pos0), kBK));
+        const int64_t full_hi = min(floor_div(static_cast<int64_t>(first_pos) - (kBK - 1) - k_pos0, kBK) + 1,
+                                    floor_div(zero_hi, kBK));
+        const int run_lo = static_cast<int>(max<int64_t>(full_lo - 1, tile_beg));
+        const int run_hi = static_cast<int>(min<int64_t>(full_hi - 1, tile_end - 3));
+        W2Run rn;
+        {
+            // every field wave-uniform and in SGPRs (the asm takes them as such)
+            auto u = [](auto x) { return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(x))); };
+            const uint64_t kp = reinterpret_cast<uint64_t>(kpool), vp = reinterpret_cast<uint64_t>(vpool);
+            rn.kbase = u(lds0);
+            rn.m0k = u(lds0 + wave * T::kInstr * 1024);
+            rn.m0v = u(lds0 + kW2VRing + wave * T::vInstr * 1024);
+            rn.pages = pages;
+            rn.kplo = u(kp), rn.kphi = u(kp >> 32);
+            rn.vdlo = u(vp - kp), rn.vdhi = u((vp - kp) >> 32);
+            rn.pbytes = u(static_cast<unsigned>(T::kRowBytes) << log2P);
+            rn.npg = num_pages;
+            rn.lastlp = u(n_pages - 1);
+            rn.log2p = u(log2P);
+            rn.pmask = u((1u << log2P) - 1);
+        }
+        for (int jt = tile_beg;;) {
+            const bool odd = ((jt - tile_beg) & 1) != 0;
             if (jt + 1 >= tile_end) {
                 W2Step s;
                 s.kslot = lds0;
                 s.vslot = sk * kW2Slot;
-                w2_last_x(m0, m1, l0, l1, ad, s, scale_log2);
+                if (odd)
+                    w2_last_y(m0, m1, l0, l1, ad, s, scale_log2);
+                else
+                    w2_last_x(m0, m1, l0, l1, ad, s, scale_log2);
                 break;
             }
-            {
-                const unsigned vs1 = sk == 2 ? 0 : sk + 1;   // V slot of tile jt+1
-                const W2Step s = step(jt);
+            if (jt >= run_lo && jt + 2 <= run_hi) {
+                unsigned cnt = static_cast<unsigned>(run_hi - jt), kk = static_cast<unsigned>((jt + 3) * kBK);
+                int idk = pg[3], idv = pg[2];
+                w2_run(m0, m1, l0, l1, ad, rn, static_cast<unsigned>((jt - tile_beg) % 6), cnt, kk, idk, idv,
+                       scale_log2);
+                jt = run_hi;
+                pg[2] = jt + 2 < tile_end ? idv : -1;
+                pg[3] = jt + 3 < tile_end ? idk : -1;
+                sk = static_cast<unsigned>((jt - tile_beg) % 3);
+                continue;
+            }
+            const unsigned vs1 = sk == 2 ? 0 : sk + 1;   // V slot of tile jt+1
+            const W2Step s = step(jt);
+            if (odd)
+                w2_tile_yx(m0, m1, l0, l1, ad, s, mask(jt + 1), scale_log2);
+            else
                 w2_tile_xy(m0, m1, l0, l1, ad, s, mask(jt + 1), scale_log2);
-                if (edge_tile(jt + 1)) {
-                    fixup(vs1, jt + 1);
-                    __syncthreads();
-                }
+            if (edge_tile(jt + 1)) {
+                fixup(vs1, jt + 1);
+                __syncthreads();
             }
-            if (jt + 2 >= tile_end) {
-                W2Step s;
-                s.kslot = lds0;
-                s.vslot = sk * kW2Slot;
-                w2_last_y(m0, m1, l0, l1, ad, s, scale_log2);
-                break;
-            }
-            {
-                const unsigned vs1 = sk == 2 ? 0 : sk + 1;   // V slot of tile jt+2
-                const W2Step s = step(jt + 1);
-                w2_tile_yx(m0, m1, l0, l1, ad, s, mask(jt + 2), scale_log2);
-                if (edge_tile(jt + 2)) {
-                    fixup(vs1, jt + 2);
-                    __syncthreads();
-                }
-            }
+            ++jt;
         }
     }
 

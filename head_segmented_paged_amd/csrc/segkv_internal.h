@@ -22,11 +22,13 @@ constexpr int kWaveRows = 32;
 // same K/V tiles, so each staged tile feeds twice the MFMAs. Either way a CU
 // holds eight waves, two per SIMD. Eight-wave units start and finish a whole
 // CU at once, which costs more than the shared staging saves when the units'
-// K/V runs are short: they are used from a mean of kWideMinKeys visible keys
-// per query row (and KV head) of the layer.
+// K/V runs are short: they are used from a mean of wide_min_keys(head_dim)
+// visible keys per query row (and KV head) of the layer. Head dim 128 runs its
+// eight-wave-shaped units on the two-block kernel, whose per-unit start is
+// cheaper, so it switches earlier.
 constexpr int kWaves = 4;
 constexpr int kWideWaves = 8;
-constexpr int64_t kWideMinKeys = 2048;
+inline int64_t wide_min_keys(int head_dim) { return head_dim == 128 ? 1536 : 2048; }
 inline int unit_waves(int page_size, bool long_context)
 {
     return page_size >= kKvTile && long_context ? kWideWaves : kWaves;

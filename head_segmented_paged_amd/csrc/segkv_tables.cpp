@@ -77,7 +77,8 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         }
     }
     const int waves =
-        segkv::unit_waves(P, vis_rows > 0.0 && vis_keys >= static_cast<double>(segkv::kWideMinKeys) * vis_rows);
+        segkv::unit_waves(P, vis_rows > 0.0 &&
+                                    vis_keys >= static_cast<double>(segkv::wide_min_keys(cfg.head_dim)) * vis_rows);
     const segkv::UnitShape shape = decode ? segkv::decode_shape(G) : segkv::unit_shape(G, waves);
     std::vector<Seg> segs;
     segs.reserve(static_cast<size_t>(S) * hkv);
