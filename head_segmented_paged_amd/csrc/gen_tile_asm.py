@@ -76,15 +76,28 @@ RING0, NRING = 64, 6        # operand ring v[64:87]
 TMP0 = 116                  # temporaries v116..v127
 LOOKAHEAD = 4               # operand reads issued this many operands ahead
 KADDR, VADDR = 88, 96       # per-tile LDS operand addresses
-DMA_AFTER = (1, 3, 5, 7, 9, 11, 13, 15)   # the tile's DMA instructions follow these MFMAs
+DMA_AFTER = (1, 3, 5, 7, 9, 11, 13, 15, 19)   # the tile's DMA groups follow these MFMAs (a ninth: scalar work)
 KB_BYTES = 32 * 256         # 32 K rows of 128 bf16
 DB_BYTES = 32 * 128         # 32 V^T rows of 64 bf16
 NEG_INF = "0xff800000"
 SLACK_LOG2 = "0x41000000"   # 8.0: refresh the running maximum only beyond this
 # K operands (two S MFMAs each) issued before each group of P.V operands
 # (t = 0..3); the 16 K operands in total.
-S_SPLIT = (6, 5, 5, 0)
+S_SPLIT = (9, 3, 4, 0)
 HAZ_MFMA_VALU = 12          # instructions between an MFMA and a VALU read of its result
+WAIT_GROUP = 2              # one counted LDS wait covers this many operands
+CAP = 6                     # issue slots that hide beside one 32x32x16 MFMA (v_exp_f32 takes two)
+
+
+def weight(line):
+    """Issue slots of one instruction line."""
+    op = line.split()[0] if line else ""
+    if op == "v_exp_f32":
+        return 2
+    if op == "s_nop":
+        return int(line.split()[1]) + 1
+    return 0 if (not op or op.endswith(":")) else 1
+PAD2 = "@pad2 "             # post item prefix: two wait states after the previous post item
 
 
 def T(i):
@@ -143,12 +156,16 @@ def addr_lines(k=True, v=True):
 
 def dma_lines(i):
     """DMA instruction i of the tile (0-3: the K tile, 4-7: the V^T tile), 1 KB
-    per wave instruction: lane l's 16 bytes land at M0 + 16 l."""
+    per wave instruction: lane l's 16 bytes land at M0 + 1024 (i % 4) + 16 l.
+    The instruction offset moves both the source and the LDS address, so M0
+    is written once per tile (K, then V^T) and the lane offsets kd / vd hold
+    the source offset minus 1024 (i % 4)."""
+    j = i % 4
     if i < 4:
-        return [f"s_add_u32 m0, %[m0k], {i * 1024}", "s_nop 0",
-                f"buffer_load_dwordx4 %[kd{i}], %[rk], %[sok] offen lds"]
-    return [f"s_add_u32 m0, %[m0v], {(i - 4) * 1024}", "s_nop 0",
-            f"buffer_load_dwordx4 %[vd{i - 4}], %[rv], %[sov] offen lds"]
+        load = f"buffer_load_dwordx4 %[kd{j}], %[rk], %[sok] offen offset:{1024 * j} lds"
+        return ["s_mov_b32 m0, %[m0k]", "s_nop 0", load] if j == 0 else [load]
+    load = f"buffer_load_dwordx4 %[vd{j}], %[rv], %[sov] offen offset:{1024 * j} lds"
+    return ["s_mov_b32 m0, %[m0v]", "s_nop 0", load] if j == 0 else [load]
 
 
 def mfma_texts(op, slot, cur, nxt):
@@ -214,10 +231,8 @@ def max_items(s_set):
             items += [(a, 1), (b, 1)]
         items += [(f"v_maximum3_f32 {ta}, {ta}, {tb}, {tb}", 1),
                   (f"v_mov_b32 {tb}, {ta}", 1),
-                  ("s_nop 1", 2),
-                  (f"v_permlane32_swap_b32 {ta}, {tb}", 1),
-                  ("s_nop 1", 2),
-                  (f"v_maximum3_f32 {ta}, {ta}, {tb}, {tb}", 1),
+                  (f"{PAD2}v_permlane32_swap_b32 {ta}, {tb}", 1),
+                  (f"{PAD2}v_maximum3_f32 {ta}, {ta}, {tb}, {tb}", 1),
                   (f"v_mul_f32 {T(4 + qb)}, %[scale], {ta}", 1)]
     return items
 
@@ -306,14 +321,23 @@ def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail, head=(), koff=0, vo
         ei += 1
         return wt
 
+    last_post = [-10]          # line index of the previous post item's last line
+
     def take_post():
         nonlocal pi
         text, wt = post_q[pi]
+        if text.startswith(PAD2):
+            text = text[len(PAD2):]
+            gap = len(lines) - 1 - last_post[0]     # instructions since the previous item
+            if gap < 2:
+                lines.append(f"s_nop {1 - gap}")
         lines.extend(text.split("\n"))
+        last_post[0] = len(lines) - 1
         pi += 1
         return wt
 
     issued = 0
+    covered = -1               # operand reads known complete
     for i in range(min(LOOKAHEAD, n)):
         lines.append(read_text(ops[i], slots[i], koff, voff))
         issued += 1
@@ -327,9 +351,12 @@ def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail, head=(), koff=0, vo
                 if len(lines) - p_written.get(base, -10) < 2:
                     lines.append("s_nop 1")
                     break
-        lines.append(f"s_waitcnt lgkmcnt({min(issued - 1 - i, 15)})")
+        if covered < i:
+            covered = min(i + WAIT_GROUP - 1, issued - 1)
+            lines.append(f"s_waitcnt lgkmcnt({min(issued - 1 - covered, 15)})")
         for k, mt in enumerate(mfma_texts(op, slots[i], cur, nxt)):
             lines.append(mt)
+            mark = len(lines)
             mfma_no += 1
             if k == 0 and i + LOOKAHEAD < n:
                 j = i + LOOKAHEAD
@@ -339,27 +366,36 @@ def schedule(ops, exp_q, post_q, final, cur, nxt, dma, tail, head=(), koff=0, vo
                 s_end_at = len(lines)
             if pending_dma and mfma_no - 1 >= DMA_AFTER[len(dma) - len(pending_dma)]:
                 lines.extend(pending_dma.pop(0))
-            # this slot's share
-            left = 2 * n - mfma_no + 1
-            rest_exp = sum(v[1] for v in exp_q[ei:])
-            rest_post = sum(v[1] for v in post_q[pi:])
-            share = math.ceil((rest_exp + rest_post) / left)
+            # issue slots left beside this MFMA: CAP less what is already
+            # placed after it (read, DMA) and the next operand's wait
+            used = sum(weight(ln) for ln in lines[mark:])
+            if k == 1 and i + 1 < n and covered < i + 1:
+                used += 1
+            share = max(0, CAP - used)
             # exponentials the next deadline needs by now
             need = 0
             nxt_t = next((o.exp_t for o in ops[i + 1:] if o.exp_t is not None and ei < done_at[o.exp_t]), None)
             if nxt_t is not None:
                 dl = next(j for j in range(i + 1, n) if ops[j].exp_t == nxt_t)
-                slots_left = 2 * (dl - i) - (1 if k == 0 else 0) - 1
+                # finished an MFMA early: no padding between the last bf16
+                # pack and the MFMA that reads it
+                slots_left = 2 * (dl - i) - (1 if k == 0 else 0) - 2
                 due = sum(v[1] for v in exp_q[ei:done_at[nxt_t]])
                 need = math.ceil(due / max(slots_left, 1))
             w = 0
             while w < need and ei < len(exp_q):
                 w += take_exp()
-            while w < share and (ei < len(exp_q) or (pi < len(post_q) and post_ready())):
+            while True:
                 if pi < len(post_q) and post_ready():
+                    if w + post_q[pi][1] > share:
+                        break
                     w += take_post()
-                else:
+                elif ei < len(exp_q):
+                    if w + exp_q[ei][1] > share:
+                        break
                     w += take_exp()
+                else:
+                    break
     while ei < len(exp_q):
         take_exp()
     while pi < len(post_q):
@@ -432,23 +468,34 @@ RSRC_WORD3 = "0x20000"
 
 def run_dma(u):
     """The eight DMA groups of run body u (K tile into K slot u % 3, V^T tile
-    into V slot (u + 2) % 3), each with one scalar instruction of the next
-    page-id load or the loop count between the M0 write and the DMA."""
-    fill = ["s_add_u32 s80, %[kk], 64",           # first key of tile j+4
-            "s_lshr_b32 s80, s80, %[log2p]",       # its page-list index
-            "s_min_u32 s80, s80, %[lastlp]",
-            "s_lshl_b32 s80, s80, 2",
-            "s_load_dword s82, %[pages], s80",
-            "s_add_u32 %[kk], %[kk], 64",
-            "s_sub_u32 %[cnt], %[cnt], 1",
-            "s_nop 0"]
+    into V slot (u + 2) % 3, M0 written before the first of each four, the
+    instruction offset moving source and destination as in dma_lines), with
+    the scalar work of the next page-id load and the loop count beside them."""
+    fill = [["s_add_u32 s80, %[kk], 64"],          # first key of tile j+4
+            ["s_lshr_b32 s80, s80, %[log2p]"],     # its page-list index
+            ["s_min_u32 s80, s80, %[lastlp]"],
+            ["s_lshl_b32 s80, s80, 2"],
+            ["s_load_dword s82, %[pages], s80"],
+            ["s_add_u32 %[kk], %[kk], 64"],
+            ["s_sub_u32 %[cnt], %[cnt], 1"],
+            []]
+    # once the last V^T DMA has read s[92:95] and s83: the next body's V^T
+    # tile is this body's K tile (resource moved to the V^T pool)
+    after_v = ["s_add_u32 s92, s88, %[vdlo]",
+               "s_addc_u32 s93, s89, %[vdhi]",
+               "s_mov_b32 s94, s90",
+               "s_lshr_b32 s83, s84, 7",
+               "s_mov_b32 %[idv], %[idk]"]
     groups = []
     for i in range(4):
-        groups.append([f"s_add_u32 m0, %[m0k], {(u % 3) * 16384 + i * 1024}", fill[i],
-                       f"buffer_load_dwordx4 %[kd{i}], {KQ}, s84 offen lds"])
+        load = f"buffer_load_dwordx4 %[kd{i}], {KQ}, s84 offen offset:{1024 * i} lds"
+        groups.append(([f"s_add_u32 m0, %[m0k], {(u % 3) * 16384}"] + fill[i] + [load]) if i == 0 else
+                      (fill[i] + [load]))
     for i in range(4):
-        groups.append([f"s_add_u32 m0, %[m0v], {((u + 2) % 3) * 16384 + i * 1024}", fill[4 + i],
-                       f"buffer_load_dwordx4 %[vd{i}], {VQ}, s83 offen lds"])
+        load = f"buffer_load_dwordx4 %[vd{i}], {VQ}, s83 offen offset:{1024 * i} lds"
+        groups.append(([f"s_add_u32 m0, %[m0v], {((u + 2) % 3) * 16384}"] + fill[4 + i] + [load]) if i == 0 else
+                      (fill[4 + i] + [load]))
+    groups.append(after_v)
     return groups
 
 
@@ -475,27 +522,22 @@ def run_body(u):
             "s_cselect_b32 s90, %[pbytes], 0",
             "s_and_b32 s84, %[kk], %[pmask]",
             "s_lshl_b32 s84, s84, 8"]
-    final = [f"v_sub_f32 {T(6)}, {T(4)}, %[m0]",
-             f"v_sub_f32 {T(7)}, {T(5)}, %[m1]",
-             f"v_max_f32 {T(6)}, {T(6)}, {T(7)}",
-             f"v_cmp_lt_f32 vcc, {SLACK_LOG2}, {T(6)}",
-             f"s_cbranch_vccnz .Lw2r{u}_%=",
+    post = max_items(nxt) + [(f"v_sub_f32 {T(6)}, {T(4)}, %[m0]", 1),
+                             (f"v_sub_f32 {T(7)}, {T(5)}, %[m1]", 1),
+                             (f"v_max_f32 {T(6)}, {T(6)}, {T(7)}", 1),
+                             (f"v_cmp_lt_f32 vcc, {SLACK_LOG2}, {T(6)}", 1)]
+    final = [f"s_cbranch_vccnz .Lw2r{u}_%=",
              f".Lw2k{u}_%=:"]
     # next body's ids and V^T resource (this tile's K resource, moved to the
     # V^T pool), then the usual wait + barrier, and the exit test
     tail = ["s_waitcnt lgkmcnt(0)",
-            "s_mov_b32 %[idv], %[idk]",
             "s_mov_b32 %[idk], s82",
-            "s_add_u32 s92, s88, %[vdlo]",
-            "s_addc_u32 s93, s89, %[vdhi]",
-            "s_mov_b32 s94, s90",
-            "s_lshr_b32 s83, s84, 7",
             "s_cmp_eq_u32 %[cnt], 0",
             "s_waitcnt vmcnt(8)",
             "s_barrier",
             "s_cbranch_scc1 .Lw2end_%="]
     lines = [f".Lw2b{u}_%=:"]
-    return lines + schedule(ops, exp_q, max_items(nxt), final, cur, nxt, run_dma(u), tail, head=head,
+    return lines + schedule(ops, exp_q, post, final, cur, nxt, run_dma(u), tail, head=head,
                             koff=((u + 1) % 3) * 16384, voff=(u % 3) * 16384)
 
 

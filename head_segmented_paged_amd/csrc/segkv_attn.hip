@@ -811,7 +811,7 @@ constexpr unsigned kW2Lds = 6 * kW2Slot;
 struct W2Addr {
     unsigned ka[8];          // K operand of k-step s: LDS byte offset within a K slot (lane's row and chunk)
     unsigned va[4];          // V^T operand of 16-key step t: LDS address within V slot 0
-    unsigned kd[4], vd[4];   // the lane's DMA source offsets within a K / V page (bytes)
+    unsigned kd[4], vd[4];   // the lane's DMA source offsets within a K / V page (bytes), less 1024 i
 };
 // Per-tile scalars of the tile bodies (wave-uniform).
 struct W2Step {
@@ -958,13 +958,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     for (int i = 0; i < T::kInstr; ++i) {
         const int p = (wave * T::kInstr + i) * 1024 + lane * 16;
         const int rr = p / T::kRowBytes, c = ((p % T::kRowBytes) / 16) ^ kswz<D>(rr);
-        ad.kd[i] = static_cast<unsigned>(rr * T::kRowBytes + c * 16);
+        ad.kd[i] = static_cast<unsigned>(rr * T::kRowBytes + c * 16 - 1024 * i);
     }
 #pragma unroll
     for (int i = 0; i < T::vInstr; ++i) {
         const int p = (wave * T::vInstr + i) * 1024 + lane * 16;
         const int d = p / 128, c = ((p % 128) / 16) ^ vswz(d);
-        ad.vd[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2);
+        ad.vd[i] = static_cast<unsigned>(((d << log2P) + c * 8) * 2 - 1024 * i);
     }
     {
         const int krow = swizzle_row(col);
@@ -993,13 +993,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         const __amdgpu_buffer_rsrc_t rk = k_rsrc(page);
 #pragma unroll
         for (int i = 0; i < T::kInstr; ++i)
-            dma16(rk, smem + slot * kW2Slot + (wave * T::kInstr + i) * 1024, ad.kd[i], slot0(jt) * T::kRowBytes);
+            dma16(rk, smem + slot * kW2Slot + (wave * T::kInstr + i) * 1024, ad.kd[i] + 1024 * i,
+                  slot0(jt) * T::kRowBytes);
     };
     auto dma_v = [&](unsigned slot, int page, int jt) {
         const __amdgpu_buffer_rsrc_t rv = v_rsrc(page);
 #pragma unroll
         for (int i = 0; i < T::vInstr; ++i)
-            dma16(rv, smem + kW2VRing + slot * kW2Slot + (wave * T::vInstr + i) * 1024, ad.vd[i], slot0(jt) * 2);
+            dma16(rv, smem + kW2VRing + slot * kW2Slot + (wave * T::vInstr + i) * 1024, ad.vd[i] + 1024 * i,
+                  slot0(jt) * 2);
     };
     auto edge_tile = [&](int jt) {
         const int key0 = jt * kBK;
