@@ -156,9 +156,13 @@ extern "C" int segkv_rope_realign(const segkv_ctx *ctx, const int32_t *entries, 
     return segkv::launch_rope_realign(ctx->cfg, entries, n, rope_base, stream);
 }
 
-extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
-                                  int32_t o_dtype, float *lse, float softmax_scale, void *workspace,
-                                  int64_t workspace_bytes, void *stream)
+namespace {
+
+// segkv_attn_prefill; with noalloc the workspace is the library's scratch
+// (workspace / workspace_bytes ignored).
+int attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o, int32_t o_dtype,
+                 float *lse, float softmax_scale, void *workspace, int64_t workspace_bytes, void *stream,
+                 bool noalloc)
 {
     segkv::clear_error();
     if (!ctx || !t) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null argument");
@@ -188,11 +192,34 @@ extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *
         if (t->num_merges > 0 && !t->merge) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null merge list");
         const int64_t need =
             static_cast<int64_t>(t->num_parts) * SEGKV_PART_BYTES(t->unit_rows, t->unit_heads, cfg.head_dim);
-        if (!workspace || workspace_bytes < need)
+        if (noalloc) {
+            if (need > SEGKV_NOALLOC_SCRATCH_BYTES)
+                return fail(SEGKV_ERR_CAPACITY, "attn_prefill_noalloc: workspace of %lld bytes needed, the "
+                            "scratch holds %lld", static_cast<long long>(need),
+                            static_cast<long long>(SEGKV_NOALLOC_SCRATCH_BYTES));
+            const int rc = segkv::noalloc_scratch(&workspace);
+            if (rc != SEGKV_OK) return rc;
+        } else if (!workspace || workspace_bytes < need) {
             return fail(SEGKV_ERR_CAPACITY, "attn_prefill: workspace of %lld bytes needed, %lld given",
                         static_cast<long long>(need), static_cast<long long>(workspace ? workspace_bytes : 0));
+        }
     }
     float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
     const float scale_log2 = scale * 1.44269504088896340736f;  // scores enter exp2 pre-multiplied by log2(e)
     return segkv::launch_attn_prefill(cfg, *t, q, o, o_dtype, lse, scale_log2, workspace, stream);
+}
+
+}  // namespace
+
+extern "C" int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
+                                  int32_t o_dtype, float *lse, float softmax_scale, void *workspace,
+                                  int64_t workspace_bytes, void *stream)
+{
+    return attn_prefill(ctx, t, q, o, o_dtype, lse, softmax_scale, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int segkv_attn_prefill_noalloc(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
+                                          int32_t o_dtype, float *lse, float softmax_scale, void *stream)
+{
+    return attn_prefill(ctx, t, q, o, o_dtype, lse, softmax_scale, nullptr, 0, stream, true);
 }

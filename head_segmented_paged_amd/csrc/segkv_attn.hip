@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "segkv_internal.h"
@@ -1914,6 +1915,34 @@ int launch_attn_mass(const segkv_config &cfg, const segkv_dev_tables &t, const v
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_mass: %s", hipGetErrorString(err));
+    return SEGKV_OK;
+}
+
+// Split-KV workspace of segkv_attn_prefill_noalloc: one array per device,
+// allocated with the code object. In host code `scratch` only names the
+// symbol; kernels get the address noalloc_scratch looks up.
+static __device__ __align__(256) unsigned char scratch[SEGKV_NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch(void **out)
+{
+    constexpr int kMaxDevices = 256;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SEGKV_ERR_UNSUPPORTED, "attn_prefill_noalloc: device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SEGKV_ERR_HIP, "attn_prefill_noalloc: scratch address on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
     return SEGKV_OK;
 }
 

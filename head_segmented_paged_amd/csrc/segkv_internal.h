@@ -93,5 +93,8 @@ int launch_attn_mass(const segkv_config &cfg, const segkv_dev_tables &t, const v
                      float scale_log2, float *mass, void *stream);
 int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o,
                         int32_t o_dtype, float *lse, float scale_log2, void *workspace, void *stream);
+// Device address of the library's no-alloc scratch on the current device
+// (SEGKV_NOALLOC_SCRATCH_BYTES), looked up on the first call per device.
+int noalloc_scratch(void **out);
 
 }  // namespace segkv

@@ -22,6 +22,7 @@ SEGKV_ERR_HIP = -4
 SEGKV_ERR_UNSUPPORTED = -5
 SEGKV_DTYPE_F32 = 0
 SEGKV_DTYPE_BF16 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SEGKV_NOALLOC_SCRATCH_BYTES
 SEG_FIELDS = 8
 UNIT_FIELDS = 8
 MERGE_FIELDS = 8
@@ -85,6 +86,8 @@ def _load():
                                     ctypes.c_int),
         "segkv_attn_prefill": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P, _i64,
                                 _P], ctypes.c_int),
+        "segkv_attn_prefill_noalloc": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, _i32, _P, ctypes.c_float, _P],
+                                       ctypes.c_int),
         "segkv_gather_pages": ([_P, _P, _i64, _P, _P, _P], ctypes.c_int),
         "segkv_rope_realign": ([_P, _P, _i64, ctypes.c_float, _P], ctypes.c_int),
         "segkv_attn_mass": ([_P, ctypes.POINTER(segkv_dev_tables), _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
@@ -102,7 +105,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("segkv_create", "segkv_destroy", "segkv_write_pages", "segkv_build_head_tables",
-            "segkv_attn_prefill", "segkv_attn_mass", "segkv_select_tokens", "segkv_sparse_ffn", "segkv_gather_pages",
+            "segkv_attn_prefill", "segkv_attn_prefill_noalloc", "segkv_attn_mass", "segkv_select_tokens", "segkv_sparse_ffn", "segkv_gather_pages",
             "segkv_rope_realign", "segkv_last_error", "segkv_version")
 
 
@@ -268,6 +271,21 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
                                    _ptr(lse), float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segkv_attn_prefill_noalloc(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None):
+    """segkv_attn_prefill with the split-KV workspace taken from the library's
+    own device scratch (NOALLOC_SCRATCH_BYTES per GPU): no allocation by the
+    call; calls that overlap on one GPU race."""
+    import torch
+    if o.dtype == torch.float32:
+        dt = SEGKV_DTYPE_F32
+    elif o.dtype == torch.bfloat16:
+        dt = SEGKV_DTYPE_BF16
+    else:
+        raise TypeError("o must be float32 or bfloat16")
+    _check(_lib.segkv_attn_prefill_noalloc(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
+                                           _ptr(lse), float(softmax_scale), _stream(stream)))
 
 
 def segkv_attn_mass(ctx, dev_tables, q, lse, mass, softmax_scale=0.0, stream=None):

@@ -285,6 +285,25 @@ int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const vo
                        int64_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * segkv_attn_prefill with the split-KV workspace taken from scratch memory
+ * the library itself holds, SEGKV_NOALLOC_SCRATCH_BYTES of device memory on
+ * every GPU it runs on, kept until the process ends. Arguments, results and
+ * errors are segkv_attn_prefill's otherwise; tables whose workspace exceeds
+ * SEGKV_NOALLOC_SCRATCH_BYTES (t->num_parts * SEGKV_PART_BYTES(...)) are
+ * refused with SEGKV_ERR_CAPACITY before anything runs. Calls no allocator.
+ * All calls on one GPU share that GPU's scratch, which keeps the last call's
+ * partial results (nothing in it needs clearing): calls that overlap on one
+ * GPU (several streams or threads) race, so the caller serialises them. The
+ * first call on a device, with that device current, looks up the scratch's
+ * device address (SEGKV_ERR_HIP if that fails).
+ */
+#define SEGKV_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int segkv_attn_prefill_noalloc(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q, void *o,
+                               int32_t o_dtype, float *lse, float softmax_scale, void *stream);
+
+/*
  * Attention mass of the step's new tokens (RedKnot summary page, "Sparse
  * FFN": only the tokens with the highest attention scores run the dense
  * FFN; this is the score). Run after segkv_attn_prefill on the same tables
