@@ -8,9 +8,10 @@ tables are bit-exact (tests/test_tables_vs_oracle.py); the paged write is
 bit-exact against the oracle's own scatter. Outputs are bitwise invariant
 under physical page relabelling, reruns and NaN-poisoned free slots.
 
-Small cases run every query; full-size workloads run sampled rows (first
-and last rows, window-edge and page-boundary rows, seeded-uniform rows),
-which the oracle computes one by one.
+Small cases, the 8K layer and the chunked varlen batch run every query; the
+32K layer and the 128K stack (two layers of each class) run sampled rows
+(first and last rows, window-edge and page-boundary rows, 256 seeded-uniform
+rows per head), which the oracle computes one by one.
 """
 
 import os
@@ -194,10 +195,11 @@ def test_decode_32k_all_rows():
     assert gl.host["num_parts"] > 0
 
 
-def test_mistral_8k_sampled():
-    """The 8K layer is split automatically (its longest block exceeds the mean
-    load per workgroup slot)."""
-    o, lse, gl = run_case(MISTRAL_8K, queries="sampled", seed=2)
+def test_mistral_8k_all_rows():
+    """The 8K layer, every row of every head (about 3.5e8 visible pairs for
+    the oracle); split automatically (its longest block exceeds the mean load
+    per workgroup slot)."""
+    o, lse, gl = run_case(MISTRAL_8K, queries="all")
     assert gl.host["num_parts"] > 0
 
 
@@ -205,36 +207,57 @@ def test_llama70b_32k_sampled():
     run_case(LLAMA70B_32K, queries="sampled", seed=3)
 
 
-def test_varlen_chunked_sampled():
-    run_case(VARLEN_CHUNKED, queries="sampled", seed=5)
+def test_varlen_chunked_all_rows():
+    """16 sequences, 2048-row chunks over cached prefixes: every row of every
+    head (about 3.4e9 visible pairs for the oracle); then the bf16 output
+    equals the fp32 output rounded to nearest even."""
+    o, lse, gl = run_case(VARLEN_CHUNKED, queries="all")
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
 
 
 def _stack_layers():
+    """Two layers of every class of the 128K stack (0, 1, 2 and 3 global KV
+    heads: the first two of each), or all 64 with SEGKV_FULL_STACK=1."""
     r = realize(STACK64_128K)
     g = r.head_class.sum(axis=1)
     if os.environ.get("SEGKV_FULL_STACK") == "1":
         return list(range(STACK64_128K.layers))
-    pick = {0, 7, 8, int(np.argmax(g)), 63}
+    pick = []
+    for c in sorted(set(g.tolist())):
+        pick += [int(i) for i in np.nonzero(g == c)[0][:2]]
     return sorted(pick)
 
 
-def test_stack128k_sampled_layers():
+_STACK_G = realize(STACK64_128K).head_class.sum(axis=1)
+
+
+@pytest.mark.parametrize("layer", _stack_layers(), ids=lambda l: f"layer{l}_g{int(_STACK_G[l])}")
+def test_stack128k_sampled_layer(layer):
+    """One layer of the 64-layer 128K stack, sampled rows of every head (256
+    seeded-uniform rows per head plus the first/last, window-edge and
+    page-boundary rows), fp32 output against the oracle; then the bf16
+    output the bench times (same kernel, bf16 store) equals the fp32 output
+    rounded to nearest even, bit for bit."""
     w = STACK64_128K
     r = realize(w)
     pools = device_pools(r.num_pages, w.page, w.d)
-    for layer in _stack_layers():
-        say(f"[case] {w.name} layer {layer} globals {int(r.head_class[layer].sum())}")
-        t = layer_tensors(w, r, layer, device="cuda")
-        gl = GpuLayer(w, r, layer, t, pools=pools)
-        o, lse = gl.run(torch.float32)
-        bits = {k: host_bits(v) for k, v in t.items()}
-        del t, gl
-        q = sampled_queries(w, r, layer, seed=100 + layer, n_uniform=48)
-        oo, ol, tab = oracle_queries(w, r, layer, bits, q)
-        stats = compare(o, lse, oo, ol, q, tab, w.hkv)
-        say(f"[ok] {w.name} layer {layer}: {stats}")
-        del o, lse, bits
-        torch.cuda.empty_cache()
+    say(f"[case] {w.name} layer {layer} globals {int(r.head_class[layer].sum())}")
+    t = layer_tensors(w, r, layer, device="cuda")
+    gl = GpuLayer(w, r, layer, t, pools=pools)
+    o, lse = gl.run(torch.float32)
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+    bits = {k: host_bits(v) for k, v in t.items()}
+    del t, gl, ob
+    q = sampled_queries(w, r, layer, seed=100 + layer, n_uniform=256)
+    oo, ol, tab = oracle_queries(w, r, layer, bits, q)
+    stats = compare(o, lse, oo, ol, q, tab, w.hkv)
+    say(f"[ok] {w.name} layer {layer}: {stats}")
+    del o, lse, bits
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("w", [TINY, adhoc(hq=8, hkv=2, d=128, page=64, window=100, classes=(0, 1),
