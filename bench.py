@@ -248,7 +248,8 @@ def ffn_bench(torch, steps, warmup, tokens=8192, keep=2048, d_model=4096, d_ff=1
     x = torch.randn((tokens, d_model), device="cuda", dtype=torch.bfloat16, generator=g)
     w = [(torch.randn(shape, device="cuda", dtype=torch.float32, generator=g) / shape[1] ** 0.5).to(torch.bfloat16)
          for shape in ((d_ff, d_model), (d_ff, d_model), (d_model, d_ff))]
-    ctx = H.segkv_create(x, x, 32, 8, 128, 64, num_pages=1)
+    ctx = H.segkv_create(torch.zeros((1, 64, 128), dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros((1, 128, 64), dtype=torch.bfloat16, device="cuda"), 32, 8, 128, 64)
     rng = np.random.Generator(np.random.PCG64(5))
     sel = torch.from_numpy(np.sort(rng.choice(tokens, keep, replace=False)).astype(np.int32)).cuda()
     dense = torch.arange(tokens, dtype=torch.int32, device="cuda")
@@ -287,7 +288,7 @@ def rope_bench(torch, n_pages, steps, warmup, P=64, D=128):
     read and written once."""
     import head_segmented_paged_amd as H
     k = torch.randn((n_pages, P, D), device="cuda", dtype=torch.bfloat16)
-    v = torch.zeros((1, D, P), device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros((n_pages, D, P), device="cuda", dtype=torch.bfloat16)
     ctx = H.segkv_create(k, v, 32, 8, D, P, num_pages=n_pages)
     rng = np.random.Generator(np.random.PCG64(11))
     ent = np.stack([np.arange(n_pages), np.zeros(n_pages), np.full(n_pages, P),

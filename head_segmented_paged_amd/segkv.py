@@ -130,6 +130,34 @@ def _ptr(x):
     return ctypes.c_void_p(x.data_ptr())
 
 
+def _tensor(name, t, dtype=None, shape=None, device=None, min_numel=None):
+    """Argument check before a C call (the C side cannot see tensor sizes, and
+    a wrong size or stride there means out-of-bounds device accesses): a
+    contiguous torch tensor on the expected device, with the given dtype and
+    shape (None entries of shape are not checked). Checks only, no arithmetic."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)} (None: any)")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {min_numel}")
+    return t
+
+
+def _ctx_device(ctx):
+    """Device of the context's pools (None for stand-in pools without one)."""
+    import torch
+    return ctx.k_pool.device if isinstance(ctx.k_pool, torch.Tensor) else None
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -160,8 +188,12 @@ class Context:
 
 def segkv_create(k_pool, v_pool, num_q_heads, num_kv_heads, head_dim, page_size, num_pages=None):
     """k_pool: bf16 [num_pages][page_size][head_dim]; v_pool: bf16 [num_pages][head_dim][page_size]."""
+    import torch
     if num_pages is None:
         num_pages = k_pool.shape[0] if k_pool is not None else 0
+    if isinstance(k_pool, torch.Tensor) or isinstance(v_pool, torch.Tensor):
+        _tensor("k_pool", k_pool, torch.bfloat16, (num_pages, page_size, head_dim))
+        _tensor("v_pool", v_pool, torch.bfloat16, (num_pages, head_dim, page_size), device=k_pool.device)
     cfg = segkv_config(num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                        _ptr(k_pool) if k_pool is not None else None,
                        _ptr(v_pool) if v_pool is not None else None)
@@ -178,8 +210,15 @@ def segkv_destroy(ctx: Context):
 
 def segkv_write_pages(ctx, k_new, v_new, cu_rows, pos0, page_of, max_rows_per_seq, stream=None):
     """k_new/v_new bf16 [rows][hkv][D]; cu_rows [S+1], pos0 [S], page_of [S][hkv][max_lp]: device int32."""
+    import torch
     num_seqs = pos0.shape[0]
     max_lp = page_of.shape[-1]
+    dev, cfg = _ctx_device(ctx), ctx.cfg
+    _tensor("k_new", k_new, torch.bfloat16, (None, cfg.num_kv_heads, cfg.head_dim), dev)
+    _tensor("v_new", v_new, torch.bfloat16, tuple(k_new.shape), dev)
+    _tensor("cu_rows", cu_rows, torch.int32, (num_seqs + 1,), dev)
+    _tensor("pos0", pos0, torch.int32, (num_seqs,), dev)
+    _tensor("page_of", page_of, torch.int32, (num_seqs, cfg.num_kv_heads, max_lp), dev)
     _check(_lib.segkv_write_pages(ctx.handle, _ptr(k_new), _ptr(v_new), k_new.shape[0], _ptr(cu_rows),
                                   _ptr(pos0), _ptr(page_of), num_seqs, max_lp, int(max_rows_per_seq),
                                   _stream(stream)))
@@ -252,6 +291,18 @@ def upload_tables(host, device="cuda"):
     return DevTables(host, device)
 
 
+def _attn_args(ctx, dev_tables, q, o, lse):
+    """q bf16 [rows][hq][D], o [rows][hq][D] (dtype checked by the caller),
+    lse fp32 [hq][rows] or None; rows = the tables' total_q_rows."""
+    import torch
+    rows, cfg, dev = int(dev_tables.struct.total_q_rows), ctx.cfg, _ctx_device(ctx)
+    _tensor("q", q, torch.bfloat16, (rows, cfg.num_q_heads, cfg.head_dim), dev)
+    if o is not None:
+        _tensor("o", o, None, (rows, cfg.num_q_heads, cfg.head_dim), q.device)
+    if lse is not None:
+        _tensor("lse", lse, torch.float32, (cfg.num_q_heads, rows), q.device)
+
+
 def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None, workspace=None):
     """q bf16 [rows][hq][D]; o fp32 or bf16 [rows][hq][D]; lse fp32 [hq][rows] or None.
     workspace: device buffer of at least the tables' workspace_bytes (split-KV
@@ -264,10 +315,13 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
         dt = SEGKV_DTYPE_BF16
     else:
         raise TypeError("o must be float32 or bfloat16")
+    _attn_args(ctx, dev_tables, q, o, lse)
     st = dev_tables.struct
     need = int(st.num_parts) * part_bytes(st.unit_rows, st.unit_heads, ctx.cfg.head_dim)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _tensor("workspace", workspace, device=q.device, min_numel=need // workspace.element_size())
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.segkv_attn_prefill(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
                                    _ptr(lse), float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -284,18 +338,31 @@ def segkv_attn_prefill_noalloc(ctx, dev_tables, q, o, lse=None, softmax_scale=0.
         dt = SEGKV_DTYPE_BF16
     else:
         raise TypeError("o must be float32 or bfloat16")
+    _attn_args(ctx, dev_tables, q, o, lse)
     _check(_lib.segkv_attn_prefill_noalloc(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(o), dt,
                                            _ptr(lse), float(softmax_scale), _stream(stream)))
 
 
 def segkv_attn_mass(ctx, dev_tables, q, lse, mass, softmax_scale=0.0, stream=None):
     """Attention mass of the new tokens: mass fp32 [rows], lse fp32 [hq][rows] from segkv_attn_prefill."""
+    import torch
+    rows = int(dev_tables.struct.total_q_rows)
+    _attn_args(ctx, dev_tables, q, None, lse)
+    _tensor("lse", lse, torch.float32, (ctx.cfg.num_q_heads, rows), q.device)
+    _tensor("mass", mass, torch.float32, (rows,), q.device)
     _check(_lib.segkv_attn_mass(ctx.handle, ctypes.byref(dev_tables.struct), _ptr(q), _ptr(lse),
                                 float(softmax_scale), _ptr(mass), _stream(stream)))
 
 
 def segkv_select_tokens(ctx, mass, cu_rows, keep, cu_keep, rows_out, stream=None):
     """Top-keep[b] rows of each sequence by mass (ties to the lower row), ascending, into rows_out."""
+    import torch
+    S = keep.shape[0]
+    _tensor("mass", mass, torch.float32, (None,))
+    _tensor("cu_rows", cu_rows, torch.int32, (S + 1,), mass.device)
+    _tensor("keep", keep, torch.int32, (S,), mass.device)
+    _tensor("cu_keep", cu_keep, torch.int32, (S + 1,), mass.device)
+    _tensor("rows_out", rows_out, torch.int32, (None,), mass.device)
     _check(_lib.segkv_select_tokens(ctx.handle, _ptr(mass), _ptr(cu_rows), _ptr(keep), _ptr(cu_keep),
                                     keep.shape[0], mass.shape[0], _ptr(rows_out), _stream(stream)))
 
@@ -305,8 +372,14 @@ def segkv_sparse_ffn(ctx, x, sel_rows, w_gate, w_up, w_down, h=None, stream=None
     weights bf16 [d_ff][d_model] (gate, up) and [d_model][d_ff] (down); h: bf16 workspace or None."""
     import torch
     n_sel, d_ff, d_model = sel_rows.shape[0], w_gate.shape[0], x.shape[1]
+    _tensor("x", x, torch.bfloat16, (None, d_model))
+    _tensor("sel_rows", sel_rows, torch.int32, (n_sel,), x.device)
+    _tensor("w_gate", w_gate, torch.bfloat16, (d_ff, d_model), x.device)
+    _tensor("w_up", w_up, torch.bfloat16, (d_ff, d_model), x.device)
+    _tensor("w_down", w_down, torch.bfloat16, (d_model, d_ff), x.device)
     if h is None:
         h = torch.empty((max(n_sel, 1), d_ff), dtype=torch.bfloat16, device=x.device)
+    _tensor("h", h, torch.bfloat16, (None, d_ff), x.device)
     _check(_lib.segkv_sparse_ffn(ctx.handle, _ptr(x), x.shape[0], d_model, d_ff, _ptr(sel_rows), n_sel,
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), h.numel() * h.element_size(),
                                  _stream(stream)))
@@ -314,10 +387,17 @@ def segkv_sparse_ffn(ctx, x, sel_rows, w_gate, w_up, w_down, h=None, stream=None
 
 def segkv_rope_realign(ctx, entries, rope_base=10000.0, stream=None):
     """entries: device int32 [n][4] = (page, slot0, nslots, delta); rotates those K slots in place."""
+    import torch
+    _tensor("entries", entries, torch.int32, (None, 4), _ctx_device(ctx))
     _check(_lib.segkv_rope_realign(ctx.handle, _ptr(entries), entries.shape[0], float(rope_base), _stream(stream)))
 
 
 def segkv_gather_pages(ctx, page_ids, k_out, v_out, stream=None):
     """page_ids device int32 [n]; k_out/v_out bf16 [n][P][D]."""
+    import torch
+    n, dev, cfg = page_ids.shape[0], _ctx_device(ctx), ctx.cfg
+    _tensor("page_ids", page_ids, torch.int32, (n,), dev)
+    _tensor("k_out", k_out, torch.bfloat16, (n, cfg.page_size, cfg.head_dim), dev)
+    _tensor("v_out", v_out, torch.bfloat16, (n, cfg.page_size, cfg.head_dim), dev)
     _check(_lib.segkv_gather_pages(ctx.handle, _ptr(page_ids), page_ids.shape[0], _ptr(k_out), _ptr(v_out),
                                    _stream(stream)))

@@ -181,3 +181,48 @@ def test_write_and_gather_validate_before_launch():
     assert rc == S.SEGKV_ERR_INVALID_ARG
     rc = S._lib.segkv_gather_pages(ctx.handle, 1, -1, 1, 2, None)
     assert rc == S.SEGKV_ERR_INVALID_ARG
+
+
+def test_binding_checks_tensors_before_calling():
+    """The binding refuses mis-shaped, mistyped or strided tensors before the
+    C call (the library cannot see tensor sizes; a wrong one would mean
+    out-of-bounds device accesses). CPU tensors: nothing reaches a device."""
+    import torch
+    hq, hkv, d, p, n = 4, 2, 64, 16, 10
+    kp = torch.zeros((n, p, d), dtype=torch.bfloat16)
+    vp = torch.zeros((n, d, p), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        H.segkv_create(kp, torch.zeros((n, p, d), dtype=torch.bfloat16), hq, hkv, d, p)   # V not transposed
+    with pytest.raises(TypeError):
+        H.segkv_create(kp.float(), vp, hq, hkv, d, p)
+    with pytest.raises(ValueError):
+        H.segkv_create(kp, vp.transpose(1, 2).contiguous().transpose(1, 2), hq, hkv, d, p)   # strided view
+    ctx = H.segkv_create(kp, vp, hq, hkv, d, p)
+    w = adhoc(hq=hq, hkv=hkv, d=d, page=p, window=8, classes=(1, 0), seqs=((0, 40),), seed=3)
+    r = realize(w)
+    host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0])
+    st = S.segkv_dev_tables(1 << 20, 1 << 21, 1 << 22, host["num_segments"], host["num_units"],
+                            host["num_page_entries"], host["total_q_rows"], host["unit_rows"], host["unit_heads"],
+                            None, 0, 0)
+
+    class Tables:
+        struct = st
+    rows = host["total_q_rows"]
+    q = torch.zeros((rows, hq, d), dtype=torch.bfloat16)
+    o = torch.zeros((rows, hq, d), dtype=torch.float32)
+    for bad_q in (q[:-1], q.float(), q.transpose(0, 1).contiguous().transpose(0, 1), torch.zeros((rows, hq, 2 * d))):
+        with pytest.raises((TypeError, ValueError)):
+            H.segkv_attn_prefill(ctx, Tables, bad_q, o)
+        with pytest.raises((TypeError, ValueError)):
+            H.segkv_attn_prefill_noalloc(ctx, Tables, bad_q, o)
+    with pytest.raises(ValueError):
+        H.segkv_attn_prefill(ctx, Tables, q, o[:, :2])
+    with pytest.raises(ValueError):
+        H.segkv_attn_prefill(ctx, Tables, q, o, lse=torch.zeros((rows, hq), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        H.segkv_write_pages(ctx, torch.zeros((5, hkv + 1, d), dtype=torch.bfloat16),
+                            torch.zeros((5, hkv + 1, d), dtype=torch.bfloat16),
+                            torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                            torch.zeros((1, hkv, 4), dtype=torch.int32), 5)
+    with pytest.raises(ValueError):
+        H.segkv_rope_realign(ctx, torch.zeros((3, 3), dtype=torch.int32))

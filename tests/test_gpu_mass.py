@@ -23,6 +23,13 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
+
+def _one_page_ctx(hq, hkv, D=128, P=64):
+    """A context for the token choice and the FFN, which read no pool: one-page pools."""
+    k = torch.zeros((1, P, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((1, D, P), dtype=torch.bfloat16, device="cuda")
+    return H.segkv_create(k, v, hq, hkv, D, P)
+
 def run_mass(w, max_unit_tiles=0, unit_pairs=None):
     r = realize(w)
     say(f"[case] mass {w.name} hq {w.hq} hkv {w.hkv} D {w.d} P {w.page} "
@@ -100,7 +107,7 @@ def test_select_tokens_matches_oracle(seed):
     k = np.minimum(keep, n)
     cu_keep = np.concatenate([[0], np.cumsum(k)]).astype(np.int32)
     say(f"[case] select seed {seed}: {len(n)} sequences, {cu[-1]} rows")
-    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 8, 2, 128, 64, num_pages=1)
+    ctx = _one_page_ctx(8, 2)
     dev = {name: torch.from_numpy(a).cuda() for name, a in
            (("mass", mass), ("cu", cu), ("keep", keep), ("cu_keep", cu_keep))}
     out = torch.full((int(cu_keep[-1]),), -7, dtype=torch.int32, device="cuda")
@@ -116,7 +123,7 @@ def test_mass_then_select_8k():
     from oracle.sparse_ffn import select_tokens
     got, ref = run_mass(MISTRAL_8K)
     n = got.shape[0]
-    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 32, 8, 128, 64, num_pages=1)
+    ctx = _one_page_ctx(32, 8)
     m = torch.from_numpy(got.astype(np.float32)).cuda()
     cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
     keep = torch.tensor([n // 4], dtype=torch.int32, device="cuda")
@@ -149,7 +156,7 @@ def test_sparse_ffn_matches_oracle(dm, dff, rows, nsel):
     wu = (torch.randn((dff, dm), generator=g) / dm ** 0.5).to(torch.bfloat16)
     wd = (torch.randn((dm, dff), generator=g) / dff ** 0.5).to(torch.bfloat16)
     sel = np.sort(np.random.Generator(np.random.PCG64(nsel)).choice(rows, nsel, replace=False)).astype(np.int32)
-    ctx = H.segkv_create(torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda"), 8, 2, 128, 64, num_pages=1)
+    ctx = _one_page_ctx(8, 2)
     xd = x.cuda()
     h = torch.empty((nsel, dff), dtype=torch.bfloat16, device="cuda")
     H.segkv_sparse_ffn(ctx, xd, torch.from_numpy(sel).cuda(), wg.cuda(), wu.cuda(), wd.cuda(), h)
