@@ -185,6 +185,16 @@ def algorithmic_bytes(w, r, o_bytes=2):
     return qo + kv / w.layers
 
 
+def write_path(w, r, ms_per_step):
+    """segkv_write_pages over the step: every new K and V row read once from
+    the caller's [rows][hkv][D] buffers and written once into its page, per
+    layer; GB/s against the HBM peak."""
+    rows = int(r.new_len.sum())
+    nbytes = 2 * 2 * rows * w.hkv * w.d * 2 * w.layers    # (read + write) x (K, V) x bf16
+    gbs = nbytes / (ms_per_step / 1e3) / 1e9
+    return {"bytes_per_step": nbytes, "ms_per_step": ms_per_step, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
 def cpu_baseline(res, target_s=18.0):
     """The fp64 oracle, as it stands, on a bounded sample of one layer's queries."""
     from oracle import paged as opaged
@@ -223,20 +233,46 @@ def cpu_baseline(res, target_s=18.0):
     dt = time.perf_counter() - t0
     per_head = int(max(4, min(4096, 4 * target_s / max(dt, 1e-3))))
     q, pairs = sample(per_head)
+    cores = opaged.threads()
     t0 = time.perf_counter()
     opaged.attention(kp, vp, bits["q"], tab, q)
     dt = time.perf_counter() - t0
+    # one thread, on a sample about 1/cores as large (a few seconds)
+    q1, pairs1 = sample(max(1, per_head // max(cores, 1)))
+    opaged.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        opaged.attention(kp, vp, bits["q"], tab, q1)
+        dt1 = time.perf_counter() - t0
+    finally:
+        opaged.set_threads(cores)
     del kp, vp
     return {
         "value": 4.0 * w.d * pairs / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": opaged.threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{len(q)} queries ({per_head} uniform rows per query head, all {w.hq} heads) of layer {layer} "
                    f"of {w.name}; {pairs} visible pairs in {dt:.1f} s; fp64"),
+        "cpu_model": cpu_model(),
+        "host_threads": os.cpu_count(),
         "ns_per_pair": dt / pairs * 1e9,
+        "single_thread_ns_per_pair": dt1 / pairs1 * 1e9,
+        "single_thread_sample": f"{len(q1)} queries, {pairs1} visible pairs in {dt1:.1f} s on 1 thread",
         "extrapolated_step_s": dt / pairs * res.pairs_per_step,
     }
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform string."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def ffn_bench(torch, steps, warmup, tokens=8192, keep=2048, d_model=4096, d_ff=14336):
@@ -415,6 +451,7 @@ def main():
         "ms_per_layer_step": wall * 1e3 / w.layers,
         "attn_ms_total": float(np.mean(attn_step)),
         "write_ms_total": float(np.mean(write_step)),
+        "write_path": write_path(w, res.r, float(np.mean(write_step))),
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "visible_pairs_per_step": res.pairs_per_step,
         "useful_flops_per_step": res.flops_per_step,

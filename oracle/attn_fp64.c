@@ -61,6 +61,16 @@ int oracle_threads(void)
 #endif
 }
 
+/* Sets the threads of the parallel loop (a single-thread timing); n < 1 is ignored. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static double widen_bf16(uint16_t bits)
 {
     uint32_t u = (uint32_t)bits << 16;

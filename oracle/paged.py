@@ -59,6 +59,8 @@ def load(path=_LIB):
                    P, ctypes.c_int64, ctypes.c_double, P]
     fm.restype = ctypes.c_int
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     _lib_cache[path] = lib
     return lib
 
@@ -66,6 +68,11 @@ def load(path=_LIB):
 def threads(lib_path=_LIB):
     """OpenMP threads the oracle runs on."""
     return int(load(lib_path).oracle_threads())
+
+
+def set_threads(n, lib_path=_LIB):
+    """Threads of the oracle's parallel loop from now on (timing only)."""
+    load(lib_path).oracle_set_threads(int(n))
 
 
 def bf16_bits(x) -> np.ndarray:
