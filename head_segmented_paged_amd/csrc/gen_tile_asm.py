@@ -237,17 +237,23 @@ def max_items(s_set):
     return items
 
 
-def refresh_block():
+def refresh_block(with_o=True):
     """When some lane's tile maximum (T4, T5) exceeds its running maximum by
     more than the slack: m = max(m, mt), alpha = 2^(m_old - m), l and O^T
     scaled by alpha. Wave-uniform branch; O^T may still be being written by
-    the body's last P.V MFMAs, hence the padding before reading it."""
+    the body's last P.V MFMAs, hence the padding before reading it. A unit's
+    first tile (with_o False) only sets m: l and O^T are still zero."""
     lines = [f"v_sub_f32 {T(6)}, {T(4)}, %[m0]",
              f"v_sub_f32 {T(7)}, {T(5)}, %[m1]",
              f"v_max_f32 {T(6)}, {T(6)}, {T(7)}",
              f"v_cmp_lt_f32 vcc, {SLACK_LOG2}, {T(6)}",
-             "s_cbranch_vccz .Lw2keep_%=",
-             "s_nop 7", "s_nop 7", "s_nop 7",
+             "s_cbranch_vccz .Lw2keep_%="]
+    if not with_o:
+        lines += [f"v_max_f32 %[m0], %[m0], {T(4)}",
+                  f"v_max_f32 %[m1], %[m1], {T(5)}",
+                  ".Lw2keep_%=:"]
+        return "\n".join(lines)
+    lines += ["s_nop 7", "s_nop 7", "s_nop 7",
              f"v_max_f32 {T(0)}, %[m0], {T(4)}",
              f"v_max_f32 {T(1)}, %[m1], {T(5)}",
              f"v_sub_f32 {T(6)}, %[m0], {T(0)}",
@@ -450,7 +456,7 @@ def scores_body(nxt):
     post_q = [(mask_block(nxt), 2)] + max_items(nxt)
     lines = ["s_nop 3"]   # Q^T and O^T were just written to AGPRs
     lines += addr_lines(v=False)
-    return lines + schedule(s_ops(), [], post_q, refresh_block().split("\n"), None, nxt, [], [])
+    return lines + schedule(s_ops(), [], post_q, refresh_block(with_o=False).split("\n"), None, nxt, [], [])
 
 
 # Steady-state run (w2_run): six tile bodies unrolled, one per phase of the

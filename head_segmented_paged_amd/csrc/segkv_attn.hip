@@ -901,6 +901,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
     const int zero_hi = k_len;
 
+    // Page id of tile jt (or -1): one scalar load from the segment's page
+    // list. Scalar loads keep the vector-memory counter, which the tile
+    // bodies' DMA uses, free of the compiler's own waits. The index is
+    // clamped so the load needs no branch (the unit's first ids go out at
+    // once, before the Q setup); the id is checked when its buffer resource
+    // is built, a body later.
+    auto page_at = [&](int jt) {
+        const int lp = __builtin_amdgcn_readfirstlane((jt * kBK) >> log2P);
+        const int id = __builtin_amdgcn_readfirstlane(pages[min(max(lp, 0), n_pages - 1)]);
+        return lp < 0 || lp >= n_pages ? -1 : id;
+    };
+    int pg[4];   // pages of tiles jt .. jt+3 at the top of the tile loop
+    pg[0] = page_at(tile_beg);
+    pg[1] = tile_beg + 1 < tile_end ? page_at(tile_beg + 1) : -1;
+    pg[2] = tile_beg + 2 < tile_end ? page_at(tile_beg + 2) : -1;
+    pg[3] = tile_beg + 3 < tile_end ? page_at(tile_beg + 3) : -1;
+
     // Per block: rows, positions, and whether the block exists.
     int wrow0[2], my_pos[2], lo_i[2], head[2];
     int64_t my_row[2];
@@ -943,15 +960,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     w2_zero_o();
     float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;   // running maximum (log2 domain) and sum per block
 
-    // Page id of tile jt (or -1): one scalar load from the segment's page
-    // list. Scalar loads keep the vector-memory counter, which the tile
-    // bodies' DMA uses, free of the compiler's own waits.
-    // The id is checked when its buffer resource is built, a body later.
-    auto page_at = [&](int jt) {
-        const int lp = __builtin_amdgcn_readfirstlane((jt * kBK) >> log2P);
-        if (lp < 0 || lp >= n_pages) return -1;
-        return __builtin_amdgcn_readfirstlane(pages[lp]);
-    };
 
     const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem));
     W2Addr ad;
@@ -1040,11 +1048,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     // and V(jt), and issues the DMA of K(jt+3) and V(jt+2), whose slots held
     // K(jt) and V(jt-1), read by the previous body (before its barrier).
     if (tile_beg < tile_end) {
-        int pg[4];   // pages of tiles jt .. jt+3 at the top of the loop
-        pg[0] = page_at(tile_beg);
-        pg[1] = tile_beg + 1 < tile_end ? page_at(tile_beg + 1) : -1;
-        pg[2] = tile_beg + 2 < tile_end ? page_at(tile_beg + 2) : -1;
-        pg[3] = tile_beg + 3 < tile_end ? page_at(tile_beg + 3) : -1;
         dma_k(0, pg[0], tile_beg);
         dma_v(0, pg[0], tile_beg);
         dma_k(1, pg[1], tile_beg + 1);
