@@ -38,7 +38,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # Sources whose change invalidates the committed HBM counter figures: the
 # attention kernel and the work-list order that decides its cache reuse.
-TRAFFIC_SOURCES = ("head_segmented_paged_amd/csrc/segkv_attn.hip", "head_segmented_paged_amd/csrc/segkv_tables.cpp")
+TRAFFIC_SOURCES = ("head_segmented_paged_amd/csrc/segkv_attn.hip", "head_segmented_paged_amd/csrc/segkv_tile_asm.inc",
+                   "head_segmented_paged_amd/csrc/segkv_tables.cpp")
 METRIC = "SegPagedAttention prefill TFLOP/s + ms/layer at 32K/128K; % bf16 MFMA peak"
 
 
