@@ -868,6 +868,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
     const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
+    const i32x4 unit3 = *reinterpret_cast<const i32x4 *>(urec + 8);
     const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
     const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
     const int part = unit2[SEGKV_UNIT_PART - 4];
@@ -904,19 +905,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     // Page id of tile jt (or -1): one scalar load from the segment's page
     // list. Scalar loads keep the vector-memory counter, which the tile
     // bodies' DMA uses, free of the compiler's own waits. The index is
-    // clamped so the load needs no branch (the unit's first ids go out at
-    // once, before the Q setup); the id is checked when its buffer resource
-    // is built, a body later.
+    // clamped so the load needs no branch; the id is checked when its buffer
+    // resource is built.
     auto page_at = [&](int jt) {
         const int lp = __builtin_amdgcn_readfirstlane((jt * kBK) >> log2P);
         const int id = __builtin_amdgcn_readfirstlane(pages[min(max(lp, 0), n_pages - 1)]);
         return lp < 0 || lp >= n_pages ? -1 : id;
     };
-    int pg[4];   // pages of tiles jt .. jt+3 at the top of the tile loop
-    pg[0] = page_at(tile_beg);
-    pg[1] = tile_beg + 1 < tile_end ? page_at(tile_beg + 1) : -1;
-    pg[2] = tile_beg + 2 < tile_end ? page_at(tile_beg + 2) : -1;
-    pg[3] = tile_beg + 3 < tile_end ? page_at(tile_beg + 3) : -1;
+    // Pages of tiles jt .. jt+3 at the top of the tile loop. The unit's first
+    // four come with its work record when the record's run starts at the
+    // unit's first visible tile (every unit the table builder makes), so the
+    // first K/V transfers wait for no page-list read; else from the list.
+    int pg[4];
+    if (tile_beg == run0) {
+        pg[0] = unit2[SEGKV_UNIT_PAGE0 - 4];
+        pg[1] = tile_beg + 1 < tile_end ? unit2[SEGKV_UNIT_PAGE0 + 1 - 4] : -1;
+        pg[2] = tile_beg + 2 < tile_end ? unit3[SEGKV_UNIT_PAGE0 + 2 - 8] : -1;
+        pg[3] = tile_beg + 3 < tile_end ? unit3[SEGKV_UNIT_PAGE0 + 3 - 8] : -1;
+    } else {
+        pg[0] = page_at(tile_beg);
+        pg[1] = tile_beg + 1 < tile_end ? page_at(tile_beg + 1) : -1;
+        pg[2] = tile_beg + 2 < tile_end ? page_at(tile_beg + 2) : -1;
+        pg[3] = tile_beg + 3 < tile_end ? page_at(tile_beg + 3) : -1;
+    }
 
     // Per block: rows, positions, and whether the block exists.
     int wrow0[2], my_pos[2], lo_i[2], head[2];
@@ -939,27 +950,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         }
     }
     const int wp_lo = q_pos0 + wr_first, wp_hi = q_pos0 + wr_last;
-
-    // Q^T of both blocks into its AGPRs (issued now, waited for by the
-    // prologue's barrier): a buffer over the unit's rows of Q, so a lane
-    // whose row or head does not exist reads zeros.
-    {
-        const int64_t urow0 = static_cast<int64_t>(q_row0) + row0;   // first Q row of the unit
-        const int64_t urows = max<int64_t>(0, min<int64_t>(unit_end - row0, total_q_rows - urow0));
-        const __amdgpu_buffer_rsrc_t rq =
-            page_rsrc(q + urow0 * hq * D, static_cast<int>(urows * hq * D * 2));
-        unsigned qo[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
-            qo[k] = can_load ? static_cast<unsigned>(((my_row[k] - urow0) * hq + head[k]) * D * 2 + 16 * half)
-                             : 0x80000000u;
-        }
-        w2_load_q(rq, qo[0], qo[1]);
-    }
-    w2_zero_o();
-    float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;   // running maximum (log2 domain) and sum per block
-
 
     const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(smem));
     W2Addr ad;
@@ -1012,6 +1002,37 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
             dma16(rv, smem + kW2VRing + slot * kW2Slot + (wave * T::vInstr + i) * 1024, ad.vd[i] + 1024 * i,
                   slot0(jt) * 2);
     };
+    // Q^T of both blocks into its AGPRs (issued now, waited for by the
+    // prologue's barrier): a buffer over the unit's rows of Q, so a lane
+    // whose row or head does not exist reads zeros.
+    {
+        const int64_t urow0 = static_cast<int64_t>(q_row0) + row0;   // first Q row of the unit
+        const int64_t urows = max<int64_t>(0, min<int64_t>(unit_end - row0, total_q_rows - urow0));
+        const __amdgpu_buffer_rsrc_t rq =
+            page_rsrc(q + urow0 * hq * D, static_cast<int>(urows * hq * D * 2));
+        unsigned qo[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
+            qo[k] = can_load ? static_cast<unsigned>(((my_row[k] - urow0) * hq + head[k]) * D * 2 + 16 * half)
+                             : 0x80000000u;
+        }
+        w2_load_q(rq, qo[0], qo[1]);
+    }
+    // Then the unit's first K/V tiles (Q comes from memory, while the K/V
+    // tiles are mostly still in the L2 from the neighbouring units' reads):
+    // Q and these are what the first tile's scores wait for.
+    if (tile_beg < tile_end) {
+        dma_k(0, pg[0], tile_beg);
+        dma_v(0, pg[0], tile_beg);
+        dma_k(1, pg[1], tile_beg + 1);
+        dma_v(1, pg[1], tile_beg + 1);
+        dma_k(2, pg[2], tile_beg + 2);
+    }
+    w2_zero_o();
+    float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;   // running maximum (log2 domain) and sum per block
+
+
     auto edge_tile = [&](int jt) {
         const int key0 = jt * kBK;
         return key0 < zero_lo || key0 + kBK > zero_hi;
@@ -1048,12 +1069,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     // and V(jt), and issues the DMA of K(jt+3) and V(jt+2), whose slots held
     // K(jt) and V(jt-1), read by the previous body (before its barrier).
     if (tile_beg < tile_end) {
-        dma_k(0, pg[0], tile_beg);
-        dma_v(0, pg[0], tile_beg);
-        dma_k(1, pg[1], tile_beg + 1);
-        dma_v(1, pg[1], tile_beg + 1);
-        dma_k(2, pg[2], tile_beg + 2);
-        __syncthreads();
+        // Q, K(0) and V(0) have landed for every wave (the transfers of K(1),
+        // V(1) and K(2), issued after them, may still be in flight: the
+        // counter counts down in issue order).
+        constexpr int kAfterV0 = 2 * T::kInstr + T::vInstr;
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterV0) : "memory");
+        __builtin_amdgcn_s_barrier();
         if (edge_tile(tile_beg)) fixup(0, tile_beg);   // V(jt+1) is fixed after body jt's barrier
         W2Step st;
         st.kslot = lds0;
@@ -1151,64 +1172,98 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     }
 
     // Epilogue: lane (col, half) holds O^T dims 32 db + 8 j + 4 half + i of its
-    // column of block k as the four values w2_get_o<k, db, j> returns.
+    // column of block k as the four values w2_get_o<k, db, j> returns. Stored
+    // from there, one store instruction would put 16 or 32 bytes into each of
+    // 32 rows, 32 cache lines per instruction. So each wave stages a block
+    // row-major in LDS and stores whole rows, 1 KB contiguous per instruction
+    // in a row of O, or in a run of partial-result rows.
     w2_drain();
     const float ltot[2] = {sum_halves(l0), sum_halves(l1)};
     const float mfin[2] = {m0, m1};
+    // The rings become the staging area once every wave is past its last
+    // tile and the transfers of the tiles past the run (zeros) have landed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    char *const stage = smem + wave * (kWaveRows * D * 4);   // this wave's 16 KB
     typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    // Block k through the staging area, one dim block at a time straight from
+    // its accumulators: row r at r * RB, its 16-byte chunk c at chunk position
+    // c ^ (r & 15), which spreads the 32 rows one write instruction touches
+    // over the LDS banks. Values are multiplied by sc (in fp32) and rounded
+    // to the element type; row r goes to dst0 + r * stride, rows at or past
+    // nrows do not exist.
+    auto put_rows = [&](auto k_c, auto f32_c, float sc, char *dst0, int64_t stride, int nrows) {
+        constexpr int k = decltype(k_c)::value;
+        constexpr bool F32 = decltype(f32_c)::value;
+        constexpr int EB = F32 ? 4 : 2, RB = D * EB, CH = RB / 16, RPP = 1024 / RB, NP = kWaveRows / RPP;
+        asm volatile("" ::: "memory");   // after the previous block's reads
+        auto put_db = [&](auto db_c) {
+            constexpr int db = decltype(db_c)::value;
+            float4 v[4];
+            w2_get_o<k, db, 0>(v[0].x, v[0].y, v[0].z, v[0].w);
+            w2_get_o<k, db, 1>(v[1].x, v[1].y, v[1].z, v[1].w);
+            w2_get_o<k, db, 2>(v[2].x, v[2].y, v[2].z, v[2].w);
+            w2_get_o<k, db, 3>(v[3].x, v[3].y, v[3].z, v[3].w);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int b0 = (32 * db + 8 * jj + 4 * half) * EB;   // byte offset within the row
+                char *p = stage + col * RB + (((b0 >> 4) ^ (col & 15)) << 4) + (b0 & 15);
+                const float4 x = v[jj];
+                if constexpr (F32)
+                    *reinterpret_cast<f32x4 *>(p) = f32x4{x.x * sc, x.y * sc, x.z * sc, x.w * sc};
+                else
+                    *reinterpret_cast<bf16x4 *>(p) =
+                        bf16x4{static_cast<__bf16>(x.x * sc), static_cast<__bf16>(x.y * sc),
+                               static_cast<__bf16>(x.z * sc), static_cast<__bf16>(x.w * sc)};
+            }
+        };
+        put_db(std::integral_constant<int, 0>{});
+        put_db(std::integral_constant<int, 1>{});
+        put_db(std::integral_constant<int, 2>{});
+        put_db(std::integral_constant<int, 3>{});
+        // Lanes read rows other lanes wrote: one wavefront's LDS operations
+        // complete in order, so only the compiler has to keep them so. Lane
+        // (rl, c) moves chunk c of rows rl, rl + RPP, ..., four reads in
+        // flight before their stores.
+        asm volatile("" ::: "memory");
+        const int rl = lane / CH, c = lane % CH;
+        char *g = dst0 + rl * stride + 16 * c;
+#pragma unroll
+        for (int p0 = 0; p0 < NP; p0 += 4) {
+            u32x4 x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (p0 + i) * RPP + rl;
+                x[i] = *reinterpret_cast<const u32x4 *>(stage + r * RB + ((c ^ (r & 15)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((p0 + i) * RPP + rl < nrows) *reinterpret_cast<u32x4 *>(g + (p0 + i) * RPP * stride) = x[i];
+        }
+    };
     auto finish = [&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
-        float4 v[4][4];
-        auto get = [&](auto db_c, auto j_c) {
-            constexpr int db = decltype(db_c)::value, j = decltype(j_c)::value;
-            w2_get_o<k, db, j>(v[db][j].x, v[db][j].y, v[db][j].z, v[db][j].w);
-        };
-        auto get_db = [&](auto db_c) {
-            get(db_c, std::integral_constant<int, 0>{});
-            get(db_c, std::integral_constant<int, 1>{});
-            get(db_c, std::integral_constant<int, 2>{});
-            get(db_c, std::integral_constant<int, 3>{});
-        };
-        get_db(std::integral_constant<int, 0>{});
-        get_db(std::integral_constant<int, 1>{});
-        get_db(std::integral_constant<int, 2>{});
-        get_db(std::integral_constant<int, 3>{});
         if (part >= 0) {
             constexpr int kPairs = kUnitRows * HPW;
             float *slot = parts + static_cast<int64_t>(part) * (kPairs * (D + 2));
-            const int rr = hoff[k] * kUnitRows + rblk[k] * kWaveRows + col;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    *reinterpret_cast<f32x4 *>(slot + rr * D + 32 * db + 8 * jj + 4 * half) =
-                        f32x4{v[db][jj].x, v[db][jj].y, v[db][jj].z, v[db][jj].w};
+            const int rr0 = hoff[k] * kUnitRows + rblk[k] * kWaveRows;   // the block's first slot row
+            put_rows(k_c, std::true_type{}, 1.0f, reinterpret_cast<char *>(slot + static_cast<int64_t>(rr0) * D),
+                     D * 4, kWaveRows);
             if (half == 0) {
-                slot[kPairs * D + rr] = mfin[k];
-                slot[kPairs * (D + 1) + rr] = ltot[k];
+                slot[kPairs * D + rr0 + col] = mfin[k];
+                slot[kPairs * (D + 1) + rr0 + col] = ltot[k];
             }
             return;
         }
-        if (!row_ok[k]) return;
         const float inv = ltot[k] > 0.f ? 1.0f / ltot[k] : 0.f;
-        const int64_t obase = (my_row[k] * hq + head[k]) * D;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = 32 * db + 8 * jj + 4 * half;
-                const float v0 = v[db][jj].x * inv, v1 = v[db][jj].y * inv;
-                const float v2 = v[db][jj].z * inv, v3 = v[db][jj].w * inv;
-                if constexpr (OUT_BF16) {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) =
-                        bf16x4{static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
-                               static_cast<__bf16>(v3)};
-                } else {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
-                }
-            }
-        if (lse && half == 0)
+        constexpr int EB = OUT_BF16 ? 2 : 4;
+        const int64_t grow0 = static_cast<int64_t>(q_row0) + wrow0[k];   // the block's first row of O
+        const int nrows = blk_ok[k] ? static_cast<int>(min<int64_t>(n_q - wrow0[k], total_q_rows - grow0)) : 0;
+        put_rows(k_c, std::integral_constant<bool, !OUT_BF16>{}, inv,
+                 static_cast<char *>(o) + (grow0 * hq + head[k]) * D * EB, static_cast<int64_t>(hq) * D * EB, nrows);
+        if (lse && half == 0 && row_ok[k])
             lse[static_cast<int64_t>(head[k]) * total_q_rows + my_row[k]] =
                 (mfin[k] + __log2f(ltot[k])) * 0.69314718055994530942f;
     };

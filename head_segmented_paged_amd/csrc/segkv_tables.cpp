@@ -251,9 +251,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
             const int64_t T = static_cast<int64_t>(sg.q_pos0) + sg.n_q;
             out->retain_lp[s] = sg.window == 0 ? 0 : static_cast<int32_t>(std::max<int64_t>(0, T - sg.window + 1) / P);
         }
-        const int32_t b = s / hkv;
         const int32_t *row = in->page_of + static_cast<int64_t>(s) * in->max_lp;
-        (void)b;
         std::memcpy(out->page_list + sg.page_off, row + sg.first_lp, sizeof(int32_t) * sg.n_pages);
     }
     out->cu_seqlens_q[0] = 0;
@@ -298,8 +296,14 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         w[SEGKV_UNIT_TILES] = dealt[u].tiles;
         w[SEGKV_UNIT_TILE0] = dealt[u].tile0;
         w[SEGKV_UNIT_PART] = dealt[u].part;
-        w[6] = 0;
-        w[7] = 0;
+        const Seg &sg = segs[dealt[u].seg];
+        for (int i = 0; i < 4; ++i) {
+            const int64_t lp = (static_cast<int64_t>(dealt[u].tile0) + i) * segkv::kKvTile / P;
+            w[SEGKV_UNIT_PAGE0 + i] =
+                i < dealt[u].tiles && lp < sg.n_pages ? out->page_list[sg.page_off + lp] : -1;
+        }
+        w[10] = 0;
+        w[11] = 0;
     }
     if (n_merges > 0) std::memcpy(out->merge, merges.data(), sizeof(int32_t) * merges.size());
     return SEGKV_OK;

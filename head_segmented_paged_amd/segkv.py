@@ -24,7 +24,7 @@ SEGKV_DTYPE_F32 = 0
 SEGKV_DTYPE_BF16 = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20   # SEGKV_NOALLOC_SCRATCH_BYTES
 SEG_FIELDS = 8
-UNIT_FIELDS = 8
+UNIT_FIELDS = 12
 MERGE_FIELDS = 8
 
 

@@ -94,7 +94,11 @@ enum {
     SEGKV_UNIT_TILES = 3,   /* KV tiles the unit visits: its cost, used to order the list */
     SEGKV_UNIT_TILE0 = 4,   /* first tile, counted in 64-key steps from the segment's k_pos0 */
     SEGKV_UNIT_PART = 5,    /* workspace slot of a split unit's partial result, -1 = writes O */
-    SEGKV_UNIT_FIELDS = 8   /* fields 6, 7 are zero */
+    SEGKV_UNIT_PAGE0 = 6,   /* fields 6 .. 9: page ids of the unit's tiles tile0 .. tile0+3 (-1 past its
+                               run or past the segment's pages), copies of page-list entries: the
+                               kernels start their first K/V transfers from them without first
+                               reading the page list */
+    SEGKV_UNIT_FIELDS = 12  /* fields 10, 11 are zero */
 };
 
 /* Fields of one merge entry (int32 [num_merges][SEGKV_MERGE_FIELDS]): the

@@ -88,7 +88,16 @@ def _check_work(lib, w):
     waves = _waves(w, lib)
     prefill_heads = max(h for h in (1, 2, 4, 8) if h <= waves and G % h == 0)
     assert (heads, rows) == ((G, 32 // G) if decode else (prefill_heads, 32 * waves // prefill_heads))
-    assert (work[:, 6:] == 0).all()
+    # fields 6..9: the page ids of the unit's first four tiles, read from the
+    # (oracle-checked) page list; -1 past the unit's run or the segment's pages
+    seg, t0, nt = work[:, 0].astype(np.int64), work[:, 4].astype(np.int64), work[:, 3].astype(np.int64)
+    off, n_pages = lib["cu_pages"][seg], lib["cu_pages"][seg + 1] - lib["cu_pages"][seg]
+    for i in range(4):
+        lp = (t0 + i) * 64 // w.page
+        ok = (i < nt) & (lp < n_pages)
+        want = np.where(ok, lib["page_list"][np.where(ok, off + lp, 0)], -1)
+        np.testing.assert_array_equal(work[:, 6 + i], want, err_msg=f"page of tile {i}")
+    assert (work[:, 10:] == 0).all()
     _check_order(work, _window(waves, decode))
     # blocks: every (segment, head, row) in exactly one block; a block's units
     # cut its natural run of tiles into consecutive pieces
