@@ -97,6 +97,7 @@ def weight(line):
     if op == "s_nop":
         return int(line.split()[1]) + 1
     return 0 if (not op or op.endswith(":")) else 1
+VMEM_SGPR_WAIT = 5          # wait states between a VALU write of an SGPR and a VMEM read of it
 PAD2 = "@pad2 "             # post item prefix: two wait states after the previous post item
 
 
@@ -609,7 +610,29 @@ def c_string(lines, indent="        "):
     return "\n".join(f'{indent}"{ln}\\n"' for ln in lines)
 
 
+def vmem_operand_pad(lines):
+    """A vector-memory instruction reading an SGPR that a VALU instruction
+    wrote needs VMEM_SGPR_WAIT wait states in between. The compiler may
+    write an operand's SGPRs with VALU code (v_readlane, reloading a spilled
+    value) right before a block and cannot see into it, so a block whose
+    first VMEM instruction with operands comes sooner opens with s_nop."""
+    n = 0
+    for ln in lines:
+        op = ln.split()[0] if ln.split() else ""
+        if not op or op.endswith(":"):
+            continue
+        if op.startswith(("buffer_", "global_")) and "%[" in ln:
+            break
+        n += weight(ln) if op == "s_nop" else 1
+        if n >= VMEM_SGPR_WAIT:
+            return lines
+    else:
+        return lines
+    return [f"s_nop {VMEM_SGPR_WAIT - n - 1}"] + lines
+
+
 def function(name, doc, lines, outs, ins, params, clobbers=CLOBBER, template=""):
+    lines = vmem_operand_pad(lines)
     return (f"// {doc}\n{template}"
             f"__device__ __forceinline__ void {name}({params})\n{{\n"
             f"    asm volatile(\n{c_string(lines)}\n"
