@@ -743,47 +743,113 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
     }
 
     const float ltot = sum_halves(lsum);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    // Lane (col, half) holds O^T dims 32 db + 8 jj + 4 half + i of its row as
+    // oacc[db][4 jj + i]. Stored from there, each store instruction would put
+    // 16 or 32 bytes into each of 32 rows (32 cache lines). Where the two K
+    // buffers hold 8 KB per wave (head dim 128, four waves) the rows leave
+    // through them instead: the last tile reads only its V^T buffer, and its
+    // K buffer was last read before the previous iteration's barrier. Row r
+    // of the wave is staged at r * 256 bytes, its 16-byte chunk c at chunk
+    // position c ^ (r & 15) (the 32 rows of one write instruction spread over
+    // the banks), all 128 dims in bf16 or 64 of them per pass in fp32, and
+    // stored whole: 1 KB contiguous per store instruction within a row.
+    constexpr int kStageWave = 8192;
+    constexpr bool kStaged = D == 128 && NW == 4 && T::kBytes == 2 * kStageWave;
+    auto put_rows = [&](auto f32_c, float sc, char *dst0, int64_t stride, int nrows) {
+        constexpr bool F32 = decltype(f32_c)::value;
+        constexpr int EB = F32 ? 4 : 2, RB = 256, CH = RB / 16, RPP = 1024 / RB, NP = kWaveRows / RPP;
+        constexpr int DBP = RB / (32 * EB);   // dim blocks per pass
+        char *const stage = (wave < NW / 2 ? kbuf0 : kbuf1) + (wave % (NW / 2)) * kStageWave;
+        const int rl = lane / CH, c = lane % CH;
+#pragma unroll
+        for (int p = 0; p < kDBlocks / DBP; ++p) {
+            asm volatile("" ::: "memory");   // after the previous pass's reads
+#pragma unroll
+            for (int dbl = 0; dbl < DBP; ++dbl)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int db = p * DBP + dbl;
+                    const int b0 = (32 * dbl + 8 * jj + 4 * half) * EB;   // byte offset within the row
+                    char *pp = stage + col * RB + (((b0 >> 4) ^ (col & 15)) << 4) + (b0 & 15);
+                    const float x0 = oacc[db][4 * jj] * sc, x1 = oacc[db][4 * jj + 1] * sc;
+                    const float x2 = oacc[db][4 * jj + 2] * sc, x3 = oacc[db][4 * jj + 3] * sc;
+                    if constexpr (F32)
+                        *reinterpret_cast<f32x4 *>(pp) = f32x4{x0, x1, x2, x3};
+                    else
+                        *reinterpret_cast<bf16x4 *>(pp) = bf16x4{static_cast<__bf16>(x0), static_cast<__bf16>(x1),
+                                                                 static_cast<__bf16>(x2), static_cast<__bf16>(x3)};
+                }
+            // lanes read rows other lanes wrote: one wavefront's LDS
+            // operations complete in order; only the compiler must keep them so
+            asm volatile("" ::: "memory");
+            char *g = dst0 + rl * stride + p * RB + 16 * c;
+#pragma unroll
+            for (int p0 = 0; p0 < NP; p0 += 4) {
+                u32x4 x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = (p0 + i) * RPP + rl;
+                    x[i] = *reinterpret_cast<const u32x4 *>(stage + rr * RB + ((c ^ (rr & 15)) << 4));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((p0 + i) * RPP + rl < nrows) *reinterpret_cast<u32x4 *>(g + (p0 + i) * RPP * stride) = x[i];
+            }
+        }
+    };
     if (part >= 0) {
         // Split unit: unnormalised O, running maximum and sum to its slot:
         // [pairs][D] outputs, then [pairs] maxima, then [pairs] sums, pair
         // r = (head offset) * unit rows + (row offset).
         constexpr int kPairs = kUnitRows * HPW;   // (row, head) pairs per unit
         float *slot = parts + static_cast<int64_t>(part) * (kPairs * (D + 2));
-        const int r = (wave % HPW) * kUnitRows + (wave / HPW) * kWaveRows + col;
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const int r0 = (wave % HPW) * kUnitRows + (wave / HPW) * kWaveRows;   // the wave's first slot row
+        const int r = r0 + col;
+        if constexpr (kStaged) {
+            put_rows(std::true_type{}, 1.0f, reinterpret_cast<char *>(slot + static_cast<int64_t>(r0) * D), D * 4,
+                     kWaveRows);
+        } else {
 #pragma unroll
-        for (int db = 0; db < kDBlocks; ++db)
+            for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                *reinterpret_cast<f32x4 *>(slot + r * D + 32 * db + 8 * jj + 4 * half) =
-                    f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+                for (int jj = 0; jj < 4; ++jj)
+                    *reinterpret_cast<f32x4 *>(slot + r * D + 32 * db + 8 * jj + 4 * half) =
+                        f32x4{oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+        }
         if (half == 0) {
             slot[kPairs * D + r] = m;
             slot[kPairs * (D + 1) + r] = ltot;
         }
         return;
     }
-    if (!row_ok) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    const int64_t obase = (my_row * hq + head) * D;
+    if constexpr (kStaged) {
+        constexpr int EB = OUT_BF16 ? 2 : 4;
+        const int64_t grow0 = static_cast<int64_t>(q_row0) + wrow0;   // the wave's first row of O
+        const int nrows = wave_valid ? static_cast<int>(min<int64_t>(n_q - wrow0, total_q_rows - grow0)) : 0;
+        put_rows(std::integral_constant<bool, !OUT_BF16>{}, inv,
+                 static_cast<char *>(o) + (grow0 * hq + head) * D * EB, static_cast<int64_t>(hq) * D * EB, nrows);
+    } else if (row_ok) {
+        const int64_t obase = (my_row * hq + head) * D;
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
+        for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int d0 = 32 * db + 8 * jj + 4 * half;
-            const float v0 = oacc[db][4 * jj + 0] * inv, v1 = oacc[db][4 * jj + 1] * inv;
-            const float v2 = oacc[db][4 * jj + 2] * inv, v3 = oacc[db][4 * jj + 3] * inv;
-            if constexpr (OUT_BF16) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 w = {static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
-                            static_cast<__bf16>(v3)};
-                *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) = w;
-            } else {
-                typedef float f32x4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * db + 8 * jj + 4 * half;
+                const float v0 = oacc[db][4 * jj + 0] * inv, v1 = oacc[db][4 * jj + 1] * inv;
+                const float v2 = oacc[db][4 * jj + 2] * inv, v3 = oacc[db][4 * jj + 3] * inv;
+                if constexpr (OUT_BF16) {
+                    *reinterpret_cast<bf16x4 *>(static_cast<u16 *>(o) + obase + d0) =
+                        bf16x4{static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
+                               static_cast<__bf16>(v3)};
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + obase + d0) = f32x4{v0, v1, v2, v3};
+                }
             }
-        }
-    if (lse && half == 0)
+    }
+    if (lse && half == 0 && row_ok)
         lse[static_cast<int64_t>(head) * total_q_rows + my_row] = (m + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
