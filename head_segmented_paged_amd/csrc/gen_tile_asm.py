@@ -646,14 +646,16 @@ def generate():
     # O^T = 0
     parts.append(function("w2_zero_o", "O^T accumulators to zero.",
                           [f"v_accvgpr_write_b32 a{OA + i}, 0" for i in range(128)], "", "", ""))
-    # Q^T straight from memory into its AGPRs: 16 loads in flight, no wait
-    # (the caller's barrier waits for them)
-    lines = [f"buffer_load_dwordx4 {ablk(QA + 32 * qb + 4 * st, 4)}, %[q{qb}], %[rq], 0 offen offset:{32 * st}"
+    # Q^T from the wave's LDS staging rows (row r = 32 qb + column at r * 256,
+    # 16-byte chunk c at chunk position c ^ (r & 15)): qa_s holds the lane's
+    # address for k-step s of block 0; block 1 lies 8 KB further on.
+    lines = [f"ds_read_b128 {ablk(QA + 32 * qb + 4 * st, 4)}, %[qa{st}] offset:{8192 * qb}"
              for qb in range(2) for st in range(8)]
-    parts.append(function("w2_load_q", "Q^T of both blocks into its AGPRs: lane chunk s of block qb from "
-                          "byte offset q_qb + 32 s of the buffer rq (an offset past its end reads zeros).",
-                          lines, "", '[rq] "s"(rq), [q0] "v"(q0), [q1] "v"(q1)',
-                          "__amdgpu_buffer_rsrc_t rq, unsigned q0, unsigned q1"))
+    lines.append("s_waitcnt lgkmcnt(0)")
+    parts.append(function("w2_q_from_lds", "Q^T of both blocks into its AGPRs from the wave's staging rows in LDS "
+                          "(qa_s: the lane's address of k-step s in block 0; block 1 at +8 KB).",
+                          lines, "", ", ".join(f'[qa{st}] "v"(qa[{st}])' for st in range(8)),
+                          "const unsigned (&qa)[8]"))
     parts.append(function("w2_scores_first", "A unit's first tile (K slot st.kslot): scores into set X, masked, "
                           "their maximum, the first running-maximum refresh.",
                           scores_body(XB), TILE_OUT, ADDR_IN + ", " + MASK_IN, TILE_PARAMS))

@@ -869,11 +869,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_pipe_kernel(
 // and P.V work in a fixed interleave. The loop around them (page ids, K/V
 // DMA into LDS, barriers, masking decisions) is the pipelined kernel's, with
 // four waves.
-// Dynamic LDS of the two-block kernel: a three-slot ring of K tiles, then a
-// three-slot ring of V^T tiles.
+// Dynamic LDS of the two-block kernel: a three-slot ring of K tiles, a
+// three-slot ring of V^T tiles, and the rows of Q on their way to the AGPRs.
 constexpr unsigned kW2Slot = 16384;
 constexpr unsigned kW2VRing = 3 * kW2Slot;
-constexpr unsigned kW2Lds = 6 * kW2Slot;
+constexpr unsigned kW2Q = 6 * kW2Slot;          // Q staging rows, 16 KB per wave
+constexpr unsigned kW2QWave = 16384;
+constexpr unsigned kW2Lds = kW2Q + 4 * kW2QWave;
 
 struct W2Addr {
     unsigned ka[8];          // K operand of k-step s: LDS byte offset within a K slot (lane's row and chunk)
@@ -1068,22 +1070,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
             dma16(rv, smem + kW2VRing + slot * kW2Slot + (wave * T::vInstr + i) * 1024, ad.vd[i] + 1024 * i,
                   slot0(jt) * 2);
     };
-    // Q^T of both blocks into its AGPRs (issued now, waited for by the
-    // prologue's barrier): a buffer over the unit's rows of Q, so a lane
-    // whose row or head does not exist reads zeros.
+    // Q of both blocks into the wave's LDS staging rows (issued now, waited
+    // for before the first scores), whole rows per transfer: staging row r =
+    // 32 qb + column holds that query's 256 bytes, 16-byte chunk c at chunk
+    // position c ^ (r & 15), so each 1 KB transfer reads four rows whole (8
+    // cache lines) where loads straight into the MFMA operand layout would
+    // touch 32 rows per instruction. A buffer over the unit's rows of Q: a
+    // lane whose row or head does not exist reads zeros.
+    char *const qstage = smem + kW2Q + wave * kW2QWave;
     {
         const int64_t urow0 = static_cast<int64_t>(q_row0) + row0;   // first Q row of the unit
         const int64_t urows = max<int64_t>(0, min<int64_t>(unit_end - row0, total_q_rows - urow0));
         const __amdgpu_buffer_rsrc_t rq =
             page_rsrc(q + urow0 * hq * D, static_cast<int>(urows * hq * D * 2));
-        unsigned qo[2];
+        const int rsub = lane >> 4, pos = lane & 15;   // row within the transfer's four, chunk position
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool can_load = blk_ok[k] && my_row[k] < total_q_rows;
-            qo[k] = can_load ? static_cast<unsigned>(((my_row[k] - urow0) * hq + head[k]) * D * 2 + 16 * half)
-                             : 0x80000000u;
+        for (int i = 0; i < 16; ++i) {
+            const int k = i >> 3, cc = 4 * (i & 7) + rsub;   // block, column of staging row 4 i + rsub
+            const int64_t row = static_cast<int64_t>(q_row0) + min(wrow0[k] + cc, n_q - 1);
+            const bool can_load = blk_ok[k] && row < total_q_rows;
+            const int c = pos ^ (cc & 15);
+            dma16(rq, qstage + i * 1024,
+                  can_load ? static_cast<unsigned>(((row - urow0) * hq + head[k]) * D * 2 + c * 16) : 0x80000000u, 0);
         }
-        w2_load_q(rq, qo[0], qo[1]);
     }
     // Then the unit's first K/V tiles (Q comes from memory, while the K/V
     // tiles are mostly still in the L2 from the neighbouring units' reads):
@@ -1142,6 +1151,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterV0) : "memory");
         __builtin_amdgcn_s_barrier();
         if (edge_tile(tile_beg)) fixup(0, tile_beg);   // V(jt+1) is fixed after body jt's barrier
+        {
+            // Q^T from the staging rows (this wave's transfers, landed): k-step
+            // s of block 0 for lane (col, half) is chunk 2 s + half of row col
+            unsigned qa[8];
+            const unsigned qrow = static_cast<unsigned>(reinterpret_cast<uintptr_t>(qstage)) + col * 256;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) qa[st] = qrow + (((2 * st + half) ^ (col & 15)) << 4);
+            w2_q_from_lds(qa);
+        }
         W2Step st;
         st.kslot = lds0;
         st.vslot = 0;
