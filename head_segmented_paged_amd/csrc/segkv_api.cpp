@@ -190,8 +190,9 @@ int attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const void *q,
         if (cfg.page_size < 64)
             return fail(SEGKV_ERR_UNSUPPORTED, "attn_prefill: split units need page_size >= 64");
         if (t->num_merges > 0 && !t->merge) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: null merge list");
-        const int64_t need =
-            static_cast<int64_t>(t->num_parts) * SEGKV_PART_BYTES(t->unit_rows, t->unit_heads, cfg.head_dim);
+    }
+    const int64_t need = SEGKV_WORKSPACE_BYTES(t->num_parts, t->unit_rows, t->unit_heads, cfg.head_dim);
+    if (need > 0) {
         if (noalloc) {
             if (need > SEGKV_NOALLOC_SCRATCH_BYTES)
                 return fail(SEGKV_ERR_CAPACITY, "attn_prefill_noalloc: workspace of %lld bytes needed, the "

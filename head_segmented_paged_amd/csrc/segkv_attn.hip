@@ -919,38 +919,114 @@ template <int HPW, bool OUT_BF16>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void attn_prefill_w2_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ kpool, const u16 *__restrict__ vpool, int64_t num_pages,
     int log2P, const int32_t *__restrict__ seg_desc, const int32_t *__restrict__ page_list,
-    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_segments, int32_t total_q_rows,
-    int32_t hq, float scale_log2, void *__restrict__ o, float *__restrict__ lse, float *__restrict__ parts,
-    int32_t num_parts)
+    int64_t num_page_entries, const int32_t *__restrict__ work, int32_t num_units, int32_t *__restrict__ queue,
+    int32_t num_segments, int32_t total_q_rows, int32_t hq, float scale_log2, void *__restrict__ o,
+    float *__restrict__ lse, float *__restrict__ parts, int32_t num_parts)
 {
     constexpr int D = 128, NW = 4;
     using T = DmaTile<D, NW>;
     constexpr int kUnitRows = 256 / HPW;       // rows per unit (eight 32-row blocks over HPW heads)
     static_assert(T::kBytes == kW2Slot && T::vBytes == kW2Slot, "tile bodies assume 16 KB tiles");
-    // kW2Lds bytes of dynamic LDS: the K ring, then the V^T ring. The LDS is
-    // dynamic so that the compiler's occupancy estimate does not raise the
-    // kernel's own register budget into the range the tile bodies keep their
-    // state in.
+    // kW2Lds bytes of dynamic LDS: the K ring, the V^T ring and the Q rows.
+    // The LDS is dynamic so that the compiler's occupancy estimate does not
+    // raise the kernel's own register budget into the range the tile bodies
+    // keep their state in.
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-    const int32_t *urec = work + static_cast<int64_t>(blockIdx.x) * SEGKV_UNIT_FIELDS;
+    // Persistent workgroups (when there are more units than CUs; else one
+    // unit each, queue null): workgroup w starts on unit w and then takes
+    // units from the queue of its XCD (workgroups go to the XCDs round-robin
+    // by index, and the table builder deals units so that those an XCD
+    // receives are neighbours: queue x holds the units at or past the grid
+    // whose index is x mod 8, in order), and once that queue is empty from
+    // the other XCDs' queues. The XCDs' clocks differ by up to ~10 % under
+    // this load, so a fixed share of units per XCD left the fast ones idle
+    // at the end of the launch. Wave 0 requests the next unit as the current
+    // one starts and passes it to the other waves through LDS (a word of its
+    // Q staging rows, free once it has read its Q) at the barrier after the
+    // first scores.
+    const int xq = static_cast<int>(blockIdx.x % kXcds);
+    int *const next_word = reinterpret_cast<int *>(smem + kW2Q);
+    // One lane's fetch-and-add on a queue counter. The offset is one the
+    // compiler cannot prove uniform: for a uniform address it would turn the
+    // atomic into a wave-level one and read its result at once, waiting for
+    // it there instead of where the result is used.
+    auto fetch_add = [&](int32_t *counter) {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        return atomicAdd(counter + z, 1);
+    };
+    auto steal = [&]() -> int {   // the other XCDs' queues (only at the end of the launch)
+        for (int i = 1; i < kXcds; ++i) {
+            const int y = xq + i < kXcds ? xq + i : xq + i - kXcds;
+            const int v = static_cast<int>(gridDim.x) + y + kXcds * fetch_add(queue + y);
+            if (v < num_units) return v;
+        }
+        return num_units;
+    };
+    int u = static_cast<int>(blockIdx.x);
+    for (;;) {
+    int nxt = num_units;   // the workgroup's next unit
+    // Per-unit copies the compiler cannot see through, so that nothing below
+    // is computed once before the unit loop and then held (spilled) through
+    // every unit.
+    int lane_u = threadIdx.x & 63, wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int log2P_u = log2P, hq_u = hq;
+    const u16 *q_u = q, *kpool_u = kpool, *vpool_u = vpool;
+    asm volatile("" : "+v"(lane_u), "+s"(wave_u), "+s"(log2P_u), "+s"(hq_u), "+s"(q_u), "+s"(kpool_u),
+                 "+s"(vpool_u));
+    {
+    const int log2P = log2P_u, hq = hq_u;
+    const u16 *const q = q_u, *const kpool = kpool_u, *const vpool = vpool_u;
+    const int wave = wave_u, lane = lane_u;
+    // This unit's request on the XCD's queue (wave 0, lane 0): issued once the
+    // unit's first transfers have landed (a vector-memory operation issued
+    // before them would hold up their counted wait), read when the next
+    // unit is published.
+    int claim_t = 0;
+    auto request = [&]() {
+        if (queue && wave == 0 && lane == 0) claim_t = fetch_add(queue + xq);
+    };
+    // The next unit into next_word (wave 0, lane 0).
+    auto publish = [&]() {
+        if (wave == 0 && lane == 0) {
+            int v = num_units;
+            if (queue) {
+                v = static_cast<int>(gridDim.x) + xq + kXcds * claim_t;
+                if (v >= num_units) v = steal();
+            }
+            next_word[0] = v;
+        }
+    };
+
+    const int32_t *urec = work + static_cast<int64_t>(u) * SEGKV_UNIT_FIELDS;
     const i32x4 unit = *reinterpret_cast<const i32x4 *>(urec);
     const i32x4 unit2 = *reinterpret_cast<const i32x4 *>(urec + 4);
     const i32x4 unit3 = *reinterpret_cast<const i32x4 *>(urec + 8);
     const int seg = unit[SEGKV_UNIT_SEGMENT], row0 = unit[SEGKV_UNIT_ROW0], head0 = unit[SEGKV_UNIT_HEAD0];
     const int run0 = unit2[SEGKV_UNIT_TILE0 - 4], run_len = unit[SEGKV_UNIT_TILES];
     const int part = unit2[SEGKV_UNIT_PART - 4];
-    if (seg < 0 || seg >= num_segments || part >= num_parts) return;
-    const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
-    const int q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
-    const int window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
-    const int page_off = desc[SEGKV_SEG_PAGE_OFF];
-    if (row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) return;
+    const bool seg_ok = seg >= 0 && seg < num_segments && part < num_parts;
+    int q_row0 = 0, n_q = 0, q_pos0 = 0, window = 0, k_pos0 = 0, k_len = 0, page_off = 0;
+    if (seg_ok) {
+        const int32_t *desc = seg_desc + static_cast<int64_t>(seg) * SEGKV_SEG_FIELDS;
+        q_row0 = desc[SEGKV_SEG_Q_ROW0], n_q = desc[SEGKV_SEG_N_Q], q_pos0 = desc[SEGKV_SEG_Q_POS0];
+        window = desc[SEGKV_SEG_WINDOW], k_pos0 = desc[SEGKV_SEG_K_POS0], k_len = desc[SEGKV_SEG_K_LEN];
+        page_off = desc[SEGKV_SEG_PAGE_OFF];
+    }
+    if (!seg_ok || row0 < 0 || row0 >= n_q || page_off < 0 || page_off >= num_page_entries || k_len < 1) {
+        // a record that fails its checks (none the table builder writes): skipped
+        request();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        publish();
+        __syncthreads();
+        nxt = __builtin_amdgcn_readfirstlane(next_word[0]);
+        __syncthreads();   // read by every wave before wave 0's next Q rows overwrite it
+    } else {
     int n_pages = (k_len + (1 << log2P) - 1) >> log2P;
     if (n_pages > num_page_entries - page_off) n_pages = static_cast<int>(num_page_entries - page_off);
     const int32_t *pages = page_list + page_off;
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     // The wave's two blocks: consecutive 32-row blocks of one head, or (eight
     // heads per unit) one 32-row block of two heads.
@@ -1150,6 +1226,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         constexpr int kAfterV0 = 2 * T::kInstr + T::vInstr;
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterV0) : "memory");
         __builtin_amdgcn_s_barrier();
+        request();
         if (edge_tile(tile_beg)) fixup(0, tile_beg);   // V(jt+1) is fixed after body jt's barrier
         {
             // Q^T from the staging rows (this wave's transfers, landed): k-step
@@ -1164,7 +1241,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
         st.kslot = lds0;
         st.vslot = 0;
         w2_scores_first(m0, m1, l0, l1, ad, st, mask(tile_beg), scale_log2);
+        publish();         // wave 0 has read its Q rows, where the word lies
         __syncthreads();   // K slot 0 is refilled by the first body; the fixups are visible
+        nxt = __builtin_amdgcn_readfirstlane(next_word[0]);
         unsigned sk = 0;   // K slot of tile jt (= slot of tile jt+3); V slot of jt is sk as well
         auto step = [&](int jt) {
             // scalars of the body of tile jt; the page of tile jt+4 is loaded
@@ -1253,6 +1332,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
             }
             ++jt;
         }
+    }
+
+    if (tile_beg >= tile_end) {   // no tile (no unit the builder makes): O and the partial result are zero
+        request();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        publish();
+        __syncthreads();
+        nxt = __builtin_amdgcn_readfirstlane(next_word[0]);
     }
 
     // Epilogue: lane (col, half) holds O^T dims 32 db + 8 j + 4 half + i of its
@@ -1353,6 +1440,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     };
     finish(std::integral_constant<int, 0>{});
     finish(std::integral_constant<int, 1>{});
+    }   // valid unit
+    }
+    if (nxt >= num_units) break;
+    u = nxt;
+    }
 }
 
 // Decode / small-chunk kernel (pages of at least one tile). A unit is one
@@ -1931,6 +2023,37 @@ __global__ __launch_bounds__(kThreads) void merge_parts_kernel(
     }
 }
 
+// Zeroes the persistent kernel's per-XCD queue counters ahead of it on the
+// same stream (a kernel, not a memset node, so a captured graph replays it).
+__global__ void zero_queue_kernel(int32_t *queue)
+{
+    if (threadIdx.x < kXcds) queue[threadIdx.x] = 0;
+}
+
+// Compute units of the current device, read once per device.
+int device_cus(int *cus)
+{
+    constexpr int kMaxDevices = 256;
+    static std::mutex mu;
+    static int count[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SEGKV_ERR_UNSUPPORTED, "attn_prefill: device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!count[dev]) {
+        int c = 0;
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || c <= 0)
+            return fail(SEGKV_ERR_HIP, "attn_prefill: compute unit count of device %d: %s", dev,
+                        hipGetErrorString(e));
+        count[dev] = c;
+    }
+    *cus = count[dev];
+    return SEGKV_OK;
+}
+
 int log2_of(int p)
 {
     int l = 0;
@@ -1940,7 +2063,7 @@ int log2_of(int p)
 
 template <int D, int HPW, bool OUT_BF16>
 int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, float *lse, float scale_log2,
-           float *parts, hipStream_t stream)
+           float *parts, int32_t *queue, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(t.num_units)), block(kThreads);
     const u16 *qh = static_cast<const u16 *>(q), *kp = static_cast<const u16 *>(cfg.k_pool);
@@ -1962,10 +2085,25 @@ int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, vo
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_prefill_w2_kernel<HPW, OUT_BF16>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kW2Lds);
             if (e != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: LDS attribute: %s", hipGetErrorString(e));
-            hipLaunchKernelGGL((attn_prefill_w2_kernel<HPW, OUT_BF16>), grid, dim3(4 * 64), kW2Lds, stream, qh, kp, vp,
-                               cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
-                               t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse, parts,
-                               t.num_parts);
+            // Persistent when there are more units than CUs: one workgroup
+            // per CU (a multiple of the XCD count), the rest through the
+            // per-XCD queues in the workspace, zeroed first.
+            int cus = 0;
+            const int rc = device_cus(&cus);
+            if (rc != SEGKV_OK) return rc;
+            const int slots = cus / kXcds * kXcds;
+            unsigned nwg = static_cast<unsigned>(t.num_units);
+            int32_t *qp = nullptr;
+            if (slots > 0 && t.num_units > slots) {
+                if (!queue) return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: no workspace for the work queues");
+                hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
+                nwg = static_cast<unsigned>(slots);
+                qp = queue;
+            }
+            hipLaunchKernelGGL((attn_prefill_w2_kernel<HPW, OUT_BF16>), dim3(nwg), dim3(4 * 64), kW2Lds, stream, qh,
+                               kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list, t.num_page_entries, t.work,
+                               t.num_units, qp, t.num_segments, t.total_q_rows, cfg.num_q_heads, scale_log2, o, lse,
+                               parts, t.num_parts);
         } else
             hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, HPW, OUT_BF16, kWideWaves>), grid, dim3(kWideWaves * 64),
                                0, stream, qh, kp, vp, cfg.num_pages, log2P, t.seg_desc, t.page_list,
@@ -1993,21 +2131,21 @@ int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, vo
 
 template <int D, int HPW>
 int launch_dtype(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                 float *lse, float scale_log2, float *parts, hipStream_t stream)
+                 float *lse, float scale_log2, float *parts, int32_t *queue, hipStream_t stream)
 {
-    if (o_dtype == SEGKV_DTYPE_BF16) return launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, parts, stream);
-    return launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, parts, stream);
+    if (o_dtype == SEGKV_DTYPE_BF16) return launch<D, HPW, true>(cfg, t, q, o, lse, scale_log2, parts, queue, stream);
+    return launch<D, HPW, false>(cfg, t, q, o, lse, scale_log2, parts, queue, stream);
 }
 
 template <int D>
 int launch_heads(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, void *o, int32_t o_dtype,
-                 float *lse, float scale_log2, float *parts, hipStream_t stream)
+                 float *lse, float scale_log2, float *parts, int32_t *queue, hipStream_t stream)
 {
     switch (t.unit_heads) {
-    case 8: return launch_dtype<D, 8>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
-    case 4: return launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
-    case 2: return launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
-    default: return launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, stream);
+    case 8: return launch_dtype<D, 8>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, stream);
+    case 4: return launch_dtype<D, 4>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, stream);
+    case 2: return launch_dtype<D, 2>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, stream);
+    default: return launch_dtype<D, 1>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, stream);
     }
 }
 
@@ -2093,9 +2231,15 @@ int launch_attn_prefill(const segkv_config &cfg, const segkv_dev_tables &t, cons
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     float *parts = static_cast<float *>(workspace);
+    // the work queues follow the partial results (units of 256 pairs only)
+    int32_t *queue = workspace && static_cast<int64_t>(t.unit_rows) * t.unit_heads == kWideWaves * kWaveRows
+                         ? reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                                       t.num_parts * SEGKV_PART_BYTES(t.unit_rows, t.unit_heads,
+                                                                                      cfg.head_dim))
+                         : nullptr;
     (void)hipGetLastError();   // a stale error of an earlier, unrelated call is not this call's
-    const int rc = cfg.head_dim == 128 ? launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s)
-                                       : launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, s);
+    const int rc = cfg.head_dim == 128 ? launch_heads<128>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, s)
+                                       : launch_heads<64>(cfg, t, q, o, o_dtype, lse, scale_log2, parts, queue, s);
     if (rc != SEGKV_OK) return rc;
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: %s", hipGetErrorString(err));

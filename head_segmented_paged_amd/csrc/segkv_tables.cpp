@@ -216,7 +216,7 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
     out->unit_heads = shape.heads;
     out->num_merges = n_merges;
     out->num_parts = static_cast<int32_t>(n_parts);
-    out->workspace_bytes = n_parts * SEGKV_PART_BYTES(shape.rows, shape.heads, cfg.head_dim);
+    out->workspace_bytes = SEGKV_WORKSPACE_BYTES(n_parts, shape.rows, shape.heads, cfg.head_dim);
     if (out->seg_cap < nseg || out->seq_cap < S || out->page_cap < pages || out->unit_cap < units ||
         out->merge_cap < n_merges)
         return fail(SEGKV_ERR_CAPACITY, "build_head_tables: buffers too small (need %d segments, %d sequences, "

@@ -28,9 +28,19 @@ UNIT_FIELDS = 12
 MERGE_FIELDS = 8
 
 
+QUEUE_BYTES = 256                   # SEGKV_QUEUE_BYTES
+
+
 def part_bytes(unit_rows, unit_heads, head_dim):
     """Workspace bytes per split-KV partial result (SEGKV_PART_BYTES)."""
     return 4 * unit_rows * unit_heads * (head_dim + 2)
+
+
+def workspace_bytes(num_parts, unit_rows, unit_heads, head_dim):
+    """Workspace segkv_attn_prefill needs (SEGKV_WORKSPACE_BYTES): the partial
+    results, then for units of 256 pairs the persistent kernel's work queues."""
+    queue = QUEUE_BYTES if unit_rows * unit_heads == 256 else 0
+    return num_parts * part_bytes(unit_rows, unit_heads, head_dim) + queue
 SEG_FIELD_NAMES = ("q_row0", "n_q", "q_pos0", "kv_head", "window", "k_pos0", "k_len", "page_off")
 
 _P = ctypes.c_void_p
@@ -306,8 +316,8 @@ def _attn_args(ctx, dev_tables, q, o, lse):
 def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, stream=None, workspace=None):
     """q bf16 [rows][hq][D]; o fp32 or bf16 [rows][hq][D]; lse fp32 [hq][rows] or None.
     workspace: device buffer of at least the tables' workspace_bytes (split-KV
-    partial results); when None and the tables need one, a torch buffer is
-    allocated for the call."""
+    partial results, the work queues); when None and the tables need one, a
+    torch buffer is allocated for the call."""
     import torch
     if o.dtype == torch.float32:
         dt = SEGKV_DTYPE_F32
@@ -317,7 +327,7 @@ def segkv_attn_prefill(ctx, dev_tables, q, o, lse=None, softmax_scale=0.0, strea
         raise TypeError("o must be float32 or bfloat16")
     _attn_args(ctx, dev_tables, q, o, lse)
     st = dev_tables.struct
-    need = int(st.num_parts) * part_bytes(st.unit_rows, st.unit_heads, ctx.cfg.head_dim)
+    need = workspace_bytes(int(st.num_parts), int(st.unit_rows), int(st.unit_heads), ctx.cfg.head_dim)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:

@@ -121,6 +121,16 @@ enum {
 #define SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) \
     (4 * (int64_t)(unit_rows) * (int64_t)(unit_heads) * ((int64_t)(head_dim) + 2))
 
+/* Bytes after the partial results in the workspace of tables whose units
+ * hold 256 (row, head) pairs: the work queues of the persistent attention
+ * kernel (eight per-XCD unit counters, zeroed by each call on its stream). */
+#define SEGKV_QUEUE_BYTES 256
+
+/* The workspace segkv_attn_prefill needs (the builder's workspace_bytes). */
+#define SEGKV_WORKSPACE_BYTES(num_parts, unit_rows, unit_heads, head_dim)                      \
+    ((int64_t)(num_parts) * SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) +                 \
+     ((int64_t)(unit_rows) * (int64_t)(unit_heads) == 256 ? (int64_t)SEGKV_QUEUE_BYTES : 0))
+
 typedef struct segkv_ctx segkv_ctx;
 
 /*
@@ -199,9 +209,9 @@ int segkv_write_pages(const segkv_ctx *ctx, const void *k_new, const void *v_new
  * max(16, ceil(mean / 2)) tiles is cut into equal runs of at most that many.
  * max_unit_tiles > 0 cuts every block longer than that; < 0 never splits.
  * A split block's runs become separate units with workspace slots, and one
- * merge entry per block; segkv_attn_prefill then needs workspace_bytes =
- * num_parts * SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) of device
- * workspace.
+ * merge entry per block. segkv_attn_prefill needs workspace_bytes =
+ * SEGKV_WORKSPACE_BYTES(num_parts, unit_rows, unit_heads, head_dim) of device
+ * workspace: the partial results, and for units of 256 pairs the work queues.
  */
 typedef struct segkv_table_inputs {
     int32_t num_seqs;
@@ -240,7 +250,7 @@ typedef struct segkv_tables {
     int32_t merge_cap;          /* merge entries (set by the caller) */
     int32_t num_merges;
     int32_t num_parts;          /* workspace slots */
-    int64_t workspace_bytes;    /* num_parts * SEGKV_PART_BYTES(unit_rows, unit_heads, head_dim) */
+    int64_t workspace_bytes;    /* SEGKV_WORKSPACE_BYTES(num_parts, unit_rows, unit_heads, head_dim) */
     int32_t *merge;             /* [merge_cap][SEGKV_MERGE_FIELDS] */
     int32_t *retain_lp;         /* [seg_cap] (appended), or NULL to skip */
 } segkv_tables;
@@ -271,11 +281,16 @@ typedef struct segkv_dev_tables {
  *   lse : device fp32 [hq][total_q_rows] natural-log sum of exp of the scaled
  *         scores, or NULL
  *   softmax_scale : multiplies q.k; <= 0 selects 1/sqrt(head_dim)
- *   workspace : device memory of at least
- *               t->num_parts * SEGKV_PART_BYTES(t->unit_rows, t->unit_heads, head_dim)
- *               bytes (caller-owned; may be NULL when num_parts == 0). Its
- *               contents need no initialisation and are scratch afterwards;
- *               calls that share a workspace must not overlap.
+ *   workspace : device memory of at least SEGKV_WORKSPACE_BYTES(t->num_parts,
+ *               t->unit_rows, t->unit_heads, head_dim) bytes, the builder's
+ *               workspace_bytes (caller-owned; may be NULL when that is 0).
+ *               Its contents need no initialisation and are scratch
+ *               afterwards; calls that share a workspace must not overlap.
+ *               With units of 256 pairs, head_dim 128 and pages of at least
+ *               64 keys, and more units than CUs, the kernel is persistent:
+ *               one workgroup per CU taking units from per-XCD queues in the
+ *               workspace, and from the other XCDs' queues once its own is
+ *               empty.
  * For query row t of segment s and query head h of its group, position
  * i = q_pos0 + t:  O = sum_j softmax_j(scale * q.k_j) v_j over the visible
  * keys j of i, computed with bf16 inputs, fp32 accumulation and an online
@@ -295,7 +310,7 @@ int segkv_attn_prefill(const segkv_ctx *ctx, const segkv_dev_tables *t, const vo
  * the library itself holds, SEGKV_NOALLOC_SCRATCH_BYTES of device memory on
  * every GPU it runs on, kept until the process ends. Arguments, results and
  * errors are segkv_attn_prefill's otherwise; tables whose workspace exceeds
- * SEGKV_NOALLOC_SCRATCH_BYTES (t->num_parts * SEGKV_PART_BYTES(...)) are
+ * SEGKV_NOALLOC_SCRATCH_BYTES (SEGKV_WORKSPACE_BYTES(t->num_parts, ...)) are
  * refused with SEGKV_ERR_CAPACITY before anything runs. Calls no allocator.
  * All calls on one GPU share that GPU's scratch, which keeps the last call's
  * partial results (nothing in it needs clearing): calls that overlap on one

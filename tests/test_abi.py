@@ -135,7 +135,8 @@ def test_split_tables_need_a_workspace():
     host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
                                      max_unit_tiles=2)
     assert host["num_parts"] > 0 and host["num_merges"] > 0
-    assert host["workspace_bytes"] == host["num_parts"] * 4 * host["unit_rows"] * host["unit_heads"] * (w.d + 2)
+    pairs = host["unit_rows"] * host["unit_heads"]
+    assert host["workspace_bytes"] == host["num_parts"] * 4 * pairs * (w.d + 2) + (256 if pairs == 256 else 0)
     dt = S.segkv_dev_tables(1, 2, 3, host["num_segments"], host["num_units"], host["num_page_entries"],
                             host["total_q_rows"], host["unit_rows"], host["unit_heads"], 9, host["num_merges"],
                             host["num_parts"])
@@ -226,3 +227,20 @@ def test_binding_checks_tensors_before_calling():
                             torch.zeros((1, hkv, 4), dtype=torch.int32), 5)
     with pytest.raises(ValueError):
         H.segkv_rope_realign(ctx, torch.zeros((3, 3), dtype=torch.int32))
+
+
+def test_binding_workspace_matches_builder():
+    """The binding sizes the workspace it allocates with the builder's formula:
+    the partial results, and for 256-pair units the persistent kernel's work
+    queues (SEGKV_QUEUE_BYTES)."""
+    for seqs, run in (((0, 300),), 2), (((0, 8192),), 0):
+        w = adhoc(hq=8, hkv=2, d=128, page=64, window=0, classes=(1, 1), seqs=seqs, seed=3)
+        r = realize(w)
+        ctx = _ctx(w.hq, w.hkv, w.d, w.page, r.num_pages)
+        host = H.segkv_build_head_tables(ctx, r.cached_len, r.new_len, r.head_class[0], r.window[0], r.page_of[0],
+                                         max_unit_tiles=run)
+        pairs = host["unit_rows"] * host["unit_heads"]
+        assert S.workspace_bytes(host["num_parts"], host["unit_rows"], host["unit_heads"], w.d) == \
+            host["workspace_bytes"]
+        assert (host["workspace_bytes"] % S.part_bytes(host["unit_rows"], host["unit_heads"], w.d) ==
+                (S.QUEUE_BYTES if pairs == 256 else 0))

@@ -136,7 +136,9 @@ def _check_work(lib, w):
             assert parts == list(range(m[3], m[3] + m[4]))
             seen_parts += parts
     assert sorted(seen_parts) == list(range(lib["num_parts"]))
-    assert lib["workspace_bytes"] == lib["num_parts"] * 4 * rows * heads * (w.d + 2)
+    # partial results, then (units of 256 pairs) the persistent kernel's work queues
+    queue = 256 if rows * heads == 256 else 0
+    assert lib["workspace_bytes"] == lib["num_parts"] * 4 * rows * heads * (w.d + 2) + queue
 
 
 @pytest.mark.parametrize("w", [x for x in ALL if x.layers == 1], ids=lambda w: w.name)
