@@ -191,7 +191,9 @@ class Context:
         return self.cfg.num_q_heads // self.cfg.num_kv_heads
 
     def __del__(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module's globals may already be gone; the
+        # process's end then releases the context
+        if getattr(self, "handle", None) and _lib is not None:
             _lib.segkv_destroy(self.handle)
             self.handle = None
 

@@ -163,6 +163,28 @@ def test_wide_units_all_rows(case):
     assert torch.equal(ob, o.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("run", [-1, 24], ids=["whole", "split"])
+def test_persistent_queues_sampled(run):
+    """More 256-pair units than CUs: the two-block kernel runs persistent, one
+    workgroup per CU taking the other units from its XCD's queue and, at the
+    end, from the other XCDs' queues. A global and a local head of unequal
+    unit costs, with and without split runs: sampled rows (band edges, page
+    edges, uniform) against the oracle, bf16 output = RNE(fp32), and a rerun
+    bitwise identical (which workgroup runs a unit does not change its
+    result)."""
+    w = adhoc(hq=8, hkv=2, d=128, page=64, window=1500, classes=(1, 0), seqs=((2500, 8300), (6000, 8000)),
+              seed=41 + run)
+    o, lse, gl = run_case(w, queries="sampled", seed=abs(run), max_unit_tiles=run)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert gl.host["unit_rows"] * gl.host["unit_heads"] == 256 and gl.host["num_units"] > cus
+    assert (gl.host["num_parts"] > 0) == (run > 0)
+    ob, _ = gl.attention(torch.bfloat16, with_lse=False)
+    o2, l2 = gl.attention(torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o.to(torch.bfloat16))
+    assert torch.equal(o2, o) and torch.equal(l2, lse)
+
+
 DECODE = [
     # (hq, hkv, d, page, window, classes, seqs, longest run in tiles: 0 automatic)
     (8, 2, 128, 64, 100, (0, 1), ((300, 1), (37, 5), (1000, 8), (5, 3)), 0),

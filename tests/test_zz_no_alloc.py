@@ -47,8 +47,10 @@ def test_noalloc_rejects_oversized_workspace():
     assert rc == S.SEGKV_ERR_INVALID_ARG
 
 
-# larger workspace first, then smaller: (hq, hkv, d, page, window, classes, seqs, longest run in tiles)
+# larger workspace first, then smaller: (hq, hkv, d, page, window, classes, seqs, longest run in tiles).
+# The first has more 256-pair units than CUs: its work queues sit in the scratch too.
 CASES = [
+    (8, 2, 128, 64, 1500, (1, 0), ((1000, 8300),), 64),
     (8, 2, 128, 64, 0, (1, 1), ((3000, 300),), 4),
     (4, 1, 128, 64, 500, (1,), ((900, 160),), 5),
 ]
@@ -80,4 +82,4 @@ def test_noalloc_matches_workspace_entry_point():
             assert torch.isfinite(o_ref.float()).all()
             assert torch.equal(o_na, o_ref), f"case {i} {dt}: output differs"
             assert torch.equal(lse_na, lse_ref), f"case {i} {dt}: lse differs"
-    assert sizes[1] < sizes[0]
+    assert sizes[2] < sizes[1] < sizes[0]
