@@ -1046,11 +1046,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(64))) void a
     const int zero_lo = max(0, (window ? max(0, q_pos0 - window + 1) : 0) - k_pos0);
     const int zero_hi = k_len;
 
-    // Page id of tile jt (or -1): one scalar load from the segment's page
-    // list. Scalar loads keep the vector-memory counter, which the tile
-    // bodies' DMA uses, free of the compiler's own waits. The index is
-    // clamped so the load needs no branch; the id is checked when its buffer
-    // resource is built.
+    // Page id of tile jt (or -1) from the segment's page list. Inside the
+    // unit loop the compiler makes this a vector load and waits for it at
+    // once (every DMA in flight with it); read through a constant-address
+    // pointer it becomes a scalar load, which measured slower still: the
+    // tile body then issued meanwhile counts it in its LDS waits. Only the
+    // bodies outside the steady-state runs (a unit's edges) load ids here;
+    // the runs read theirs in their own code. The index is clamped so the
+    // load needs no branch; the id is checked when its buffer resource is
+    // built.
     auto page_at = [&](int jt) {
         const int lp = __builtin_amdgcn_readfirstlane((jt * kBK) >> log2P);
         const int id = __builtin_amdgcn_readfirstlane(pages[min(max(lp, 0), n_pages - 1)]);

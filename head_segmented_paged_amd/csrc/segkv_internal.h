@@ -28,7 +28,7 @@ constexpr int kWaveRows = 32;
 // cheaper, so it switches earlier.
 constexpr int kWaves = 4;
 constexpr int kWideWaves = 8;
-inline int64_t wide_min_keys(int head_dim) { return head_dim == 128 ? 1536 : 2048; }
+inline int64_t wide_min_keys(int head_dim) { return head_dim == 128 ? 1024 : 2048; }
 inline int unit_waves(int page_size, bool long_context)
 {
     return page_size >= kKvTile && long_context ? kWideWaves : kWaves;

@@ -82,9 +82,10 @@ enum {
  * one workgroup of the attention kernel: unit_rows consecutive query rows of
  * one segment for unit_heads consecutive query heads of its GQA group, over
  * a run of the 64-key tiles those rows see. The builder picks the shape per
- * call: unit_rows * unit_heads = 128 (four waves), 256 for long contexts
- * with pages >= 64 (eight waves; a mean of at least 2048 visible keys per
- * query row and KV head), or 32 / G rows x G heads for decode steps. A block
+ * call: unit_rows * unit_heads = 128 for short contexts, 256 for long ones
+ * with pages >= 64 (a mean of at least 1024 visible keys per query row and KV
+ * head at head dim 128, 2048 at 64), or 32 / G rows x G heads for decode
+ * steps. A block
  * whose run is split into several units (split-KV) writes partial results to
  * the workspace, and one merge entry per block combines them. */
 enum {

@@ -42,12 +42,12 @@ def _compare(w, r, layer, ctx):
 
 def _waves(w, lib):
     """Wavefronts per prefill workgroup: eight for pages of at least one tile
-    when the layer's mean visible keys per query row and KV head reach 1536
+    when the layer's mean visible keys per query row and KV head reach 1024
     for head dim 128, 2048 otherwise (sum of visible pairs over its segments,
     from the oracle-checked total_pairs, against the cut x rows), four
     otherwise."""
     G = w.hq // w.hkv
-    cut = 1536 if w.d == 128 else 2048
+    cut = 1024 if w.d == 128 else 2048
     long_context = lib["total_pairs"] >= cut * G * w.hkv * lib["total_q_rows"]
     return 8 if w.page >= 64 and long_context else 4
 
