@@ -171,8 +171,13 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
             max_run = std::max<int64_t>(segkv::kDecodeMinRun, (total_tiles + target - 1) / target);
         } else {
             const int64_t slots = static_cast<int64_t>(segkv::kXcds) * segkv::cohort(waves);
+            // Runs of half a slot's mean load; the two-block kernel (head dim
+            // 128, 256-pair units), whose workgroups take units from queues
+            // until none is left, balances whole ones, and every extra run
+            // costs it a unit's start and end: runs of a slot's mean load.
+            const int64_t per = cfg.head_dim == 128 && waves == segkv::kWideWaves ? slots : 2 * slots;
             if (4 * longest * slots > 3 * total_tiles)
-                max_run = std::max<int64_t>(segkv::kMinRun, (total_tiles + 2 * slots - 1) / (2 * slots));
+                max_run = std::max<int64_t>(segkv::kMinRun, (total_tiles + per - 1) / per);
         }
     }
     std::vector<int32_t> merges;   // [num_merges][SEGKV_MERGE_FIELDS]
