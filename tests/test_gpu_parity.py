@@ -163,8 +163,17 @@ def test_wide_units_all_rows(case):
     assert torch.equal(ob, o.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("run", [-1, 24], ids=["whole", "split"])
-def test_persistent_queues_sampled(run):
+PERSISTENT = [
+    # (seqs, longest run in tiles: -1 none); 510 units, or 258: two past the
+    # CU count, so nearly every workgroup finds its queue empty at once
+    (((2500, 8300), (6000, 8000)), -1),
+    (((2500, 8300), (6000, 8000)), 24),
+    (((0, 8256),), -1),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=["whole", "split", "cus_plus_2"])
+def test_persistent_queues_sampled(case):
     """More 256-pair units than CUs: the two-block kernel runs persistent, one
     workgroup per CU taking the other units from its XCD's queue and, at the
     end, from the other XCDs' queues. A global and a local head of unequal
@@ -172,8 +181,8 @@ def test_persistent_queues_sampled(run):
     edges, uniform) against the oracle, bf16 output = RNE(fp32), and a rerun
     bitwise identical (which workgroup runs a unit does not change its
     result)."""
-    w = adhoc(hq=8, hkv=2, d=128, page=64, window=1500, classes=(1, 0), seqs=((2500, 8300), (6000, 8000)),
-              seed=41 + run)
+    seqs, run = case
+    w = adhoc(hq=8, hkv=2, d=128, page=64, window=1500, classes=(1, 0), seqs=seqs, seed=41 + run + len(seqs))
     o, lse, gl = run_case(w, queries="sampled", seed=abs(run), max_unit_tiles=run)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert gl.host["unit_rows"] * gl.host["unit_heads"] == 256 and gl.host["num_units"] > cus
