@@ -2084,8 +2084,9 @@ int launch(const segkv_config &cfg, const segkv_dev_tables &t, const void *q, vo
         return fail(SEGKV_ERR_INVALID_ARG, "attn_prefill: unsupported unit_heads %d", t.unit_heads);
     } else if (big_page && t.unit_rows * t.unit_heads == kWideWaves * kWaveRows) {
         if constexpr (D == 128) {
-            // 96 KB of dynamic LDS: above the default limit, set per launch (the
-            // attribute is per device)
+            // 160 KB of dynamic LDS: above the default limit, set per launch
+            // (the attribute is per device; setting it is allowed under graph
+            // capture)
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_prefill_w2_kernel<HPW, OUT_BF16>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kW2Lds);
             if (e != hipSuccess) return fail(SEGKV_ERR_HIP, "attn_prefill: LDS attribute: %s", hipGetErrorString(e));
