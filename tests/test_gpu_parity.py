@@ -164,15 +164,19 @@ def test_wide_units_all_rows(case):
 
 
 PERSISTENT = [
-    # (seqs, longest run in tiles: -1 none); 510 units, or 258: two past the
-    # CU count, so nearly every workgroup finds its queue empty at once
-    (((2500, 8300), (6000, 8000)), -1),
-    (((2500, 8300), (6000, 8000)), 24),
-    (((0, 8256),), -1),
+    # (hq, hkv, classes, seqs, longest run in tiles: -1 none); G = 4 with 510
+    # units, or 258: two past the CU count, so nearly every workgroup finds
+    # its queue empty at once; G = 1 (256 rows x 1 head) and G = 8 (32 rows x
+    # 8 heads) with 264
+    (8, 2, (1, 0), ((2500, 8300), (6000, 8000)), -1),
+    (8, 2, (1, 0), ((2500, 8300), (6000, 8000)), 24),
+    (8, 2, (1, 0), ((0, 8256),), -1),
+    (8, 8, (1, 0, 0, 0, 0, 0, 0, 1), ((1000, 8448),), -1),
+    (16, 2, (0, 1), ((3000, 4200),), 32),
 ]
 
 
-@pytest.mark.parametrize("case", PERSISTENT, ids=["whole", "split", "cus_plus_2"])
+@pytest.mark.parametrize("case", PERSISTENT, ids=["g4_whole", "g4_split", "g4_cus_plus_2", "g1", "g8_split"])
 def test_persistent_queues_sampled(case):
     """More 256-pair units than CUs: the two-block kernel runs persistent, one
     workgroup per CU taking the other units from its XCD's queue and, at the
@@ -181,8 +185,8 @@ def test_persistent_queues_sampled(case):
     edges, uniform) against the oracle, bf16 output = RNE(fp32), and a rerun
     bitwise identical (which workgroup runs a unit does not change its
     result)."""
-    seqs, run = case
-    w = adhoc(hq=8, hkv=2, d=128, page=64, window=1500, classes=(1, 0), seqs=seqs, seed=41 + run + len(seqs))
+    hq, hkv, classes, seqs, run = case
+    w = adhoc(hq=hq, hkv=hkv, d=128, page=64, window=1500, classes=classes, seqs=seqs, seed=41 + run + len(seqs) + hq)
     o, lse, gl = run_case(w, queries="sampled", seed=abs(run), max_unit_tiles=run)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert gl.host["unit_rows"] * gl.host["unit_heads"] == 256 and gl.host["num_units"] > cus
