@@ -285,12 +285,21 @@ extern "C" int segkv_build_head_tables(const segkv_ctx *ctx, const segkv_table_i
         // Positions base + 8j + x belong to XCD x. The XCDs take the sorted
         // window in turn, in reverse turn order every other window, so that
         // no XCD always receives the costlier end of the windows (each XCD
-        // drains only its own share of the list).
+        // drains only its own share of the list). Each XCD's share is laid
+        // out last row first: a causal head's later rows are its longer
+        // units, and the workgroups of an XCD take their next unit in the
+        // order they finish, so the one that finished first (the shortest
+        // unit) takes the longest next one. In ascending order the early
+        // finishers took the shortest again and the XCD's units drifted apart
+        // in the K/V stream over the launch (by ~200 tiles, more than the L2
+        // holds, at a 128K layer's end), and each refetched it.
         const bool reverse = (base / window) % 2 == 1;
         size_t idx = 0;
         for (int t = 0; t < segkv::kXcds; ++t) {
             const int x = reverse ? segkv::kXcds - 1 - t : t;
-            for (size_t p = x; p < n; p += segkv::kXcds) dealt[base + p] = list[base + idx++];
+            const size_t c = static_cast<size_t>(x) < n ? (n - x + segkv::kXcds - 1) / segkv::kXcds : 0;
+            for (size_t k = 0; k < c; ++k) dealt[base + x + k * segkv::kXcds] = list[base + idx + c - 1 - k];
+            idx += c;
         }
     }
     for (size_t u = 0; u < n_units; ++u) {

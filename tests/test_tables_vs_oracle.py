@@ -60,7 +60,8 @@ def _window(waves, decode):
 
 def _check_order(work, WINDOW):
     """Longest first between windows; inside a window, each XCD's share
-    (positions x, x+8, ...) in (segment, row, head) order."""
+    (positions x, x+8, ...) in descending (segment, row, head) order, and the
+    shares one after another in ascending order."""
     tiles = work[:, 3]
     for a in range(0, len(work), WINDOW):
         win = work[a:a + WINDOW]
@@ -68,16 +69,16 @@ def _check_order(work, WINDOW):
             assert tiles[a:a + WINDOW].min() >= tiles[a + WINDOW:].max()
         for x in range(8):
             share = [tuple(int(v) for v in u[[0, 1, 2, 4]]) for u in win[x::8]]
-            assert all(a < b for a, b in zip(share, share[1:]))
+            assert all(a > b for a, b in zip(share, share[1:]))
         # the XCDs' shares follow one another in (segment, row, head) order,
         # XCD 0 first in even windows and XCD 7 first in odd ones
         order = range(min(8, len(win)))
         if (a // WINDOW) % 2 == 1:
             order = [x for x in reversed(range(8)) if x < len(win)]
-        firsts = [tuple(win[x::8][0][[0, 1, 2, 4]]) for x in order]
-        lasts = [tuple(win[x::8][-1][[0, 1, 2, 4]]) for x in order]
-        for i in range(len(firsts) - 1):
-            assert lasts[i] < firsts[i + 1]
+        lows = [tuple(win[x::8][-1][[0, 1, 2, 4]]) for x in order]
+        highs = [tuple(win[x::8][0][[0, 1, 2, 4]]) for x in order]
+        for i in range(len(lows) - 1):
+            assert highs[i] < lows[i + 1]
 
 
 def _check_work(lib, w):
